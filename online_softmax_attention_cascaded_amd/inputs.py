@@ -1,0 +1,98 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module draws random numbers and rounds them once to the storage dtype; it
+holds none of the method's arithmetic. Both the oracle and the HIP path are fed
+the very same arrays. Draws use numpy's PCG64 generator
+(``numpy.random.default_rng(seed)``), ``standard_normal(dtype=float32)`` in C
+order; rounding to bf16 uses torch's CPU cast (round to nearest even).
+
+Workload shapes (synthetic stand-ins for the model workloads the pages
+measure -- attention, MoE routing and FP8 quantise-then-GEMM -- whose shapes the
+pages do not print):
+
+* tiny fp32 attention: B=1, H=1, Lq=64, Lk=256, d=64;
+* prefill: B=4, H=32, Lq=Lk=2048, d=128, bf16;
+* decode: B=8, Hq=32, Hkv=8, Lk=32768, d=128, bf16 KV cache;
+* routing: 16384 tokens x 256 experts fp32 logits, 1 % of rows with +6 on one
+  random expert;
+* FP8: A 4096 x 7168 bf16 with 0.1 % of entries scaled by 50, B source
+  4096 x 7168 bf16 (quantised per row of B, i.e. per output column).
+"""
+
+import numpy as np
+import torch
+
+
+def normal(rng, shape):
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def as_bf16(x):
+    """float32 numpy array -> bf16 torch CPU tensor (one round to nearest even)."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
+
+
+def attention_inputs(seed, B, Hq, Hkv, Lq, Lk, d, dtype=torch.bfloat16):
+    """q [B,Hq,Lq,d], k, v [B,Hkv,Lk,d] ~ N(0,1), as torch CPU tensors of ``dtype``."""
+    rng = np.random.default_rng(seed)
+    q = normal(rng, (B, Hq, Lq, d))
+    k = normal(rng, (B, Hkv, Lk, d))
+    v = normal(rng, (B, Hkv, Lk, d))
+    if dtype == torch.float32:
+        return torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)
+    return as_bf16(q), as_bf16(k), as_bf16(v)
+
+
+def decode_inputs(seed, B, Hq, Hkv, Lk, d):
+    """q [B,Hq,d], k, v [B,Hkv,Lk,d] ~ N(0,1), bf16 torch CPU tensors."""
+    rng = np.random.default_rng(seed)
+    q = as_bf16(normal(rng, (B, Hq, d)))
+    k = as_bf16(normal(rng, (B, Hkv, Lk, d)))
+    v = as_bf16(normal(rng, (B, Hkv, Lk, d)))
+    return q, k, v
+
+
+def worked_example_decode(d=128):
+    """Three keys whose scores against the single query are 1, 3 and 5 (scale 1),
+    with value rows whose first component is 2, -1 and 4; every other component
+    is 0. With two segments of ceil(3/2) = 2 keys the tiles are {1, 3} and {5}.
+    Returns bf16 torch CPU tensors q [1,1,d], k, v [1,1,3,d]."""
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 1.0
+    k = np.zeros((1, 1, 3, d), np.float32)
+    k[0, 0, :, 0] = [1.0, 3.0, 5.0]
+    v = np.zeros((1, 1, 3, d), np.float32)
+    v[0, 0, :, 0] = [2.0, -1.0, 4.0]
+    return as_bf16(q), as_bf16(k), as_bf16(v)
+
+
+def routing_inputs(seed, T, E, spike_frac=0.01, spike=6.0):
+    """fp32 logits [T, E] ~ N(0,1); round(spike_frac*T) rows, drawn without
+    replacement, get +spike on one uniformly drawn expert."""
+    rng = np.random.default_rng(seed)
+    x = normal(rng, (T, E))
+    n = int(round(spike_frac * T))
+    rows = rng.choice(T, size=n, replace=False)
+    cols = rng.integers(0, E, size=n)
+    x[rows, cols] += np.float32(spike)
+    return torch.from_numpy(x)
+
+
+def tie_heavy_logits(seed, T, E, values=(-1.0, 0.0, 1.0, 2.0)):
+    """fp32 logits drawn uniformly from a few values, so ties are everywhere."""
+    rng = np.random.default_rng(seed)
+    v = np.asarray(values, np.float32)
+    return torch.from_numpy(v[rng.integers(0, len(v), size=(T, E))])
+
+
+def quant_inputs(seed, M, N, K, outlier_frac=1e-3, outlier_scale=50.0):
+    """A [M,K] bf16 ~ N(0,1) with round(outlier_frac*M*K) entries, drawn without
+    replacement, scaled by outlier_scale before rounding; B source [N,K] bf16 ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    a = normal(rng, (M, K))
+    n = int(round(outlier_frac * M * K))
+    if n:
+        pos = rng.choice(M * K, size=n, replace=False)
+        a.reshape(-1)[pos] *= np.float32(outlier_scale)
+    b = normal(rng, (N, K))
+    return as_bf16(a), as_bf16(b)

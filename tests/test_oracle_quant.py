@@ -1,0 +1,161 @@
+"""Pins of the e4m3 codec and the abs-max -> quantise -> GEMM oracle (no GPU)."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.codec import e4m3_decode, e4m3_encode, e4m3_table
+from online_softmax_attention_cascaded_amd import inputs
+
+
+# ---------------------------------------------------------------- codec
+
+
+def test_table_landmarks_from_the_format_definition():
+    t = e4m3_table()
+    assert len(t) == 127 and np.all(np.diff(t) > 0)
+    assert t[0] == 0 and t[1] == 2.0 ** -9 and t[7] == 7 * 2.0 ** -9
+    assert t[8] == 2.0 ** -6          # smallest normal
+    assert t[0x38] == 1.0             # exponent field 7 = bias
+    assert t[0x7E] == 448.0           # largest finite
+    assert np.isnan(e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_round_trip_all_finite_codes():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    assert len(codes) == 254
+    assert np.array_equal(e4m3_encode(e4m3_decode(codes)), codes)
+
+
+@pytest.mark.parametrize(
+    "x,expect",
+    [
+        (17.0, 16.0),             # tie between 16 (even) and 18
+        (19.0, 20.0),             # tie between 18 and 20 (even)
+        (2.0 ** -10, 0.0),        # tie between 0 (even) and 2^-9
+        (1.5 * 2.0 ** -9, 2.0 ** -8),  # tie between 2^-9 and 2^-8 (even)
+        (7.5 * 2.0 ** -9, 2.0 ** -6),  # subnormal/normal boundary tie goes to the even code
+        (464.0, 448.0),           # tie with the (absent) 480 rounds down
+        (470.0, 448.0),           # saturation
+        (1e6, 448.0),
+        (-1e6, -448.0),
+        (0.3, 0.3125),            # nearest of 0.28125 and 0.3125
+    ],
+)
+def test_rounding_cases(x, expect):
+    assert e4m3_decode(e4m3_encode(np.array([x])))[0] == expect
+
+
+def test_matches_torch_cpu_cast_inside_range():
+    """Library pin: torch's float8_e4m3fn cast (round to nearest even) where it is
+    defined without saturation (|x| < 464)."""
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(200_000) * 40,
+        rng.uniform(-2 ** -5, 2 ** -5, 100_000),
+        (e4m3_table()[:-1] + e4m3_table()[1:]) / 2,       # every midpoint
+        -(e4m3_table()[:-1] + e4m3_table()[1:]) / 2,
+    ]).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    ours = e4m3_encode(x.astype(np.float64))
+    theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, theirs)
+
+
+# ---------------------------------------------------------------- quantiser
+
+
+def test_quantiser_scale_and_absmax_element():
+    a, _ = inputs.quant_inputs(1, 16, 4, 300)
+    x = a.float().numpy()
+    codes, s = oracle.absmax_quant(x)
+    amax = np.abs(x).max(axis=1)
+    assert s.dtype == np.float32
+    assert np.array_equal(s, (amax / np.float32(448)).astype(np.float32))
+    j = np.abs(x).argmax(axis=1)
+    c = codes[np.arange(16), j]
+    assert np.all((c == 0x7E) | (c == 0xFE))
+    assert np.all(np.sign(e4m3_decode(c)) == np.sign(x[np.arange(16), j]))
+
+
+def test_quantiser_error_bound():
+    """Dequantised values are within half a step of the input: relative 2^-4 in the
+    normal range, absolute 2^-10 * s below it."""
+    a, _ = inputs.quant_inputs(2, 32, 4, 512)
+    x = a.float().numpy().astype(np.float64)
+    codes, s = oracle.absmax_quant(x.astype(np.float32))
+    deq = e4m3_decode(codes) * s[:, None]
+    y = np.abs(x / s[:, None])
+    err = np.abs(deq - x)
+    normal = y >= 2.0 ** -6
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(x[normal]) * (1 + 1e-6))
+    assert np.all(err[~normal] <= (2.0 ** -10 * np.broadcast_to(s[:, None], x.shape)[~normal]) * (1 + 1e-6))
+
+
+def test_zero_row():
+    x = np.zeros((3, 10), np.float32)
+    x[1] = np.linspace(-1, 1, 10)
+    x[2, 4] = -0.0
+    codes, s = oracle.absmax_quant(x)
+    assert s[0] == 0 and s[2] == 0 and s[1] > 0
+    assert np.all(codes[0] == 0) and np.all(codes[2] == 0)
+
+
+# ---------------------------------------------------------------- GEMM
+
+
+def test_gemm_is_exact_against_integer_arithmetic():
+    a, b = inputs.quant_inputs(3, 24, 20, 1000)
+    aq, sa = oracle.absmax_quant(a.float().numpy())
+    bq, sb = oracle.absmax_quant(b.float().numpy())
+    c = oracle.quant_gemm(aq, sa, bq, sb)
+    ai = np.rint(e4m3_decode(aq) * 512).astype(np.int64)
+    bi = np.rint(e4m3_decode(bq) * 512).astype(np.int64)
+    assert np.array_equal(ai / 512, e4m3_decode(aq))
+    rng = np.random.default_rng(0)
+    for _ in range(40):
+        i, j = int(rng.integers(24)), int(rng.integers(20))
+        exact = sum(int(p) * int(r) for p, r in zip(ai[i], bi[j]))
+        ref = Fraction(exact, 2 ** 18) * Fraction(float(sa[i])) * Fraction(float(sb[j]))
+        assert abs(Fraction(c[i, j]) - ref) <= abs(ref) * Fraction(1, 2 ** 51)
+
+
+def test_gemm_transposition_pin():
+    """C_ij uses row i of A and row j of the [N, K] B operand (not its transpose)."""
+    aq = np.zeros((2, 3), np.uint8)
+    bq = np.zeros((2, 3), np.uint8)
+    aq[0, 0] = e4m3_encode(np.array([2.0]))[0]
+    bq[1, 0] = e4m3_encode(np.array([3.0]))[0]
+    c = oracle.quant_gemm(aq, np.array([1.0, 1.0]), bq, np.array([1.0, 0.5]))
+    assert c.tolist() == [[0.0, 3.0], [0.0, 0.0]]
+
+
+def test_running_scale_without_quantisation_is_the_plain_product():
+    """Transcript cue 33 in real arithmetic: rescaling the accumulator by old/new
+    abs-max whenever it grows gives exactly the unfused product."""
+    a, b = inputs.quant_inputs(5, 8, 6, 700)
+    x = a.float().numpy()
+    bq, sb = oracle.absmax_quant(b.float().numpy())
+    ref = x.astype(np.float64) @ (e4m3_decode(bq) * sb[:, None].astype(np.float64)).T
+    for kt in (64, 100, 700):
+        c = oracle.quant_gemm_running_scale(x, bq, sb, kt, quantize=False)
+        assert np.allclose(c, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_running_scale_single_tile_is_the_final_scale_path():
+    a, b = inputs.quant_inputs(6, 8, 6, 640)
+    x = a.float().numpy()
+    bq, sb = oracle.absmax_quant(b.float().numpy())
+    aq, sa = oracle.absmax_quant(x)
+    c1 = oracle.quant_gemm(aq, sa, bq, sb)
+    c2 = oracle.quant_gemm_running_scale(x, bq, sb, 640, quantize=True)
+    assert np.allclose(c1, c2, rtol=1e-15, atol=0)
+
+
+def test_outlier_generator():
+    a, _ = inputs.quant_inputs(7, 100, 2, 1000)
+    x = a.float().numpy()
+    assert (np.abs(x) > 20).sum() >= 50   # about 100 entries scaled by 50
