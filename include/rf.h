@@ -1,0 +1,162 @@
+/*
+ * rf.h -- C ABI of a small MI355X (gfx950) library that computes chains of
+ * dependent reductions ("cascaded reductions") in one pass with a running,
+ * rescaled state.
+ *
+ * The operations follow the statement of the problem on the source pages:
+ *   - attention: scores Q K^T, safe softmax, product with V, computed with a
+ *     running max m, a running denominator l and an accumulator rescaled by
+ *     exp(m_old - m_new), divided by l once at the end
+ *     ("RedFuser episode transcript", cues 9, 15, 17 and 19);
+ *   - split-KV decode: the key sequence is split into segments whose partial
+ *     states (m, l, acc) are merged by rescaling to a common max
+ *     (transcript cues 21 and 39; "RedFuser episode visual explainer",
+ *     widgets "Merging partial states across blocks (FlashDecoding-style)"
+ *     and "Single-Segment vs Multi-Segment");
+ *   - MoE routing: softmax followed by top-k (transcript cue 11;
+ *     "Online normalizer calculation for softmax", abstract);
+ *   - FP8: per-token abs-max, scale, e4m3 cast, then GEMM (transcript cue 33).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers on the current HIP device, row-major
+ *     and contiguous, 16-byte aligned unless stated otherwise. The caller
+ *     allocates and owns every buffer (including workspaces); the library
+ *     allocates nothing and keeps no state between calls.
+ *   - Outputs must not alias inputs.
+ *   - Calls only enqueue work on `stream` (0 = the null stream) and return.
+ *     All arguments are validated before anything is enqueued, so a call that
+ *     returns an error has launched nothing; kernel faults surface at the
+ *     caller's next synchronisation, as with any HIP launch.
+ *   - A call whose output is empty (a zero batch or row count) returns RF_OK
+ *     and enqueues nothing; null pointers are accepted only then.
+ *   - Calls are re-entrant; rf_last_error() is per host thread.
+ *   - Inputs are expected finite; a NaN propagates to the rows it touches.
+ */
+#ifndef RF_H_
+#define RF_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RF_ABI_VERSION 1
+
+typedef enum {
+  RF_OK = 0,
+  RF_ERR_INVALID_ARG = 1, /* null pointer, misalignment, negative size, inconsistent shape */
+  RF_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for (dtype, head size, k, K) */
+  RF_ERR_LAUNCH = 3       /* the HIP runtime refused a launch; detail in rf_last_error() */
+} rf_status;
+
+typedef enum { RF_F32 = 0, RF_BF16 = 1 } rf_dtype;
+
+/*
+ * rf_attn_fwd -- O = softmax(scale * Q K^T [+ causal mask]) V, one pass over
+ * K/V tiles with running (m, l, acc) per query row (transcript cues 15-19).
+ *
+ *   dt     RF_BF16: q, k, v, o are bf16, math in fp32 (MFMA for both
+ *          contractions); RF_F32: all fp32 (FMA). Head size d in {64, 128}.
+ *   q      [B, Hq, Lq, d]      k, v  [B, Hkv, Lk, d]     o  [B, Hq, Lq, d] (dt)
+ *   lse    [B, Hq, Lq] fp32 or NULL: m + ln(l) of the scaled scores.
+ *   Hq % Hkv == 0; query head h reads key/value head h / (Hq / Hkv).
+ *   causal != 0 masks key j for query i when j > i and needs Lq == Lk.
+ *   Lk >= 1 whenever the output is non-empty. scale is explicit (no default).
+ */
+rf_status rf_attn_fwd(rf_dtype dt, const void* q, const void* k, const void* v, void* o,
+                      float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale,
+                      int causal, hipStream_t stream);
+
+/*
+ * rf_attn_decode_split -- first half of split-KV decode (one query row per
+ * head). Keys are split into S segments of ceil(Lk / S) keys (the last ones
+ * may be shorter or empty); for every (b, query head, segment) it writes the
+ * unnormalised partial state over that segment's keys:
+ *   part_m   [B, Hq, S]     max of the scaled scores (-inf for an empty segment)
+ *   part_l   [B, Hq, S]     sum of exp(score - part_m)          (0 if empty)
+ *   part_acc [B, Hq, S, d]  sum of exp(score - part_m) * v      (0 if empty)
+ * all fp32 (transcript cue 39: Multi-Segment; cue 21: the states merge).
+ *
+ *   dt must be RF_BF16: q [B, Hq, d], k, v [B, Hkv, Lk, d] bf16; d == 128;
+ *   Hq % Hkv == 0 and Hq / Hkv <= 16; S >= 1; Lk >= 1.
+ */
+rf_status rf_attn_decode_split(rf_dtype dt, const void* q, const void* k, const void* v,
+                               float* part_m, float* part_l, float* part_acc, int B, int Hq,
+                               int Hkv, int Lk, int d, int S, float scale, hipStream_t stream);
+
+/*
+ * rf_merge_states -- second half of split-KV decode: for each of `rows` rows,
+ * merge S partial states by rescaling each to the common max m* and adding
+ * (transcript cue 21): w_s = exp(m_s - m*) (0 for m_s = -inf),
+ * l = sum w_s l_s, o = sum w_s acc_s / l, lse = m* + ln(l).
+ * A row whose states are all empty gets o = 0 and lse = -inf.
+ *
+ *   part_m, part_l [rows, S] fp32; part_acc [rows, S, d] fp32;
+ *   o [rows, d] in out_dt (RF_BF16 or RF_F32); lse [rows] fp32 or NULL.
+ *   1 <= d <= 1024, d % 4 == 0.
+ */
+rf_status rf_merge_states(const float* part_m, const float* part_l, const float* part_acc,
+                          int rows, int S, int d, rf_dtype out_dt, void* o, float* lse,
+                          hipStream_t stream);
+
+/*
+ * rf_softmax_topk -- MoE routing: per row of logits, softmax then top-k
+ * (transcript cue 11; "Online normalizer calculation for softmax", abstract),
+ * fused into one pass over the row.
+ *
+ *   logits  [T, E] fp32;  weights [T, k] fp32;  indices [T, k] int32.
+ *   Experts are ranked by logit descending, equal logits by index ascending,
+ *   and returned in that order. weights are the softmax probabilities of the
+ *   selected experts, divided by their own sum when renormalize != 0.
+ *   1 <= k <= min(E, 32); E <= 1024; E % 4 == 0.
+ */
+rf_status rf_softmax_topk(const float* logits, int T, int E, int k, int renormalize,
+                          float* weights, int32_t* indices, hipStream_t stream);
+
+/*
+ * rf_absmax_quant_fp8 -- per-row abs-max, scale and e4m3 cast (transcript
+ * cue 33, first reduction): a_i = max_k |x_ik|, s_i = fp32(a_i / 448),
+ * q_ik = e4m3(fp32(x_ik / s_i)), divisions correctly rounded, e4m3 = OCP
+ * E4M3 (no infinities, largest 448) with round-to-nearest-even after clamping
+ * the magnitude to 448. A row with a_i = 0 gets s_i = 0 and all codes 0.
+ *
+ *   x [rows, cols] bf16;  q [rows, cols] uint8 (e4m3 codes);  scale [rows] fp32.
+ *   cols % 8 == 0 and cols <= 8192; q needs only 8-byte alignment.
+ */
+rf_status rf_absmax_quant_fp8(const void* x, int rows, int cols, uint8_t* q, float* scale,
+                              hipStream_t stream);
+
+/*
+ * rf_absmax_quant_gemm_fp8 -- the FP8 cascade: quantise A per row exactly as
+ * rf_absmax_quant_fp8 does, then C_ij = bf16(s_i * t_j * sum_k A_q[i,k] B_q[j,k])
+ * with fp32 accumulation (transcript cue 33: abs-max, then the GEMM over the
+ * scaled values).
+ *
+ *   a       [M, K] bf16
+ *   b       [N, K] uint8 e4m3 codes (K contiguous; the K x N operand stored
+ *           column by column), b_scale [N] fp32 (per output column)
+ *   a_q     [M, K] uint8 workspace, written (caller-owned, 8-byte aligned)
+ *   a_scale [M] fp32, written
+ *   c       [M, N] bf16
+ *   K % 128 == 0 and K <= 8192; M, N >= 0.
+ */
+rf_status rf_absmax_quant_gemm_fp8(const void* a, const uint8_t* b, const float* b_scale, int M,
+                                   int N, int K, uint8_t* a_q, float* a_scale, void* c,
+                                   hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* rf_status_string(rf_status s);
+
+/* Detail of the last non-OK return on this host thread ("" if none). */
+const char* rf_last_error(void);
+
+/* RF_ABI_VERSION of the built library. */
+int rf_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RF_H_ */

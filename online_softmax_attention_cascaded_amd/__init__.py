@@ -1,0 +1,25 @@
+"""Cascaded reductions fused into one incremental loop, native on MI355X (gfx950).
+
+The compute lives in ``librf.so`` (hand-written HIP kernels behind a C ABI,
+``include/rf.h``); ``binding`` is the ctypes layer over it and ``inputs`` the
+seeded synthetic input generator. Importing the package does not load the
+library; the first call does, and raises if it has not been built.
+"""
+
+from .binding import (  # noqa: F401
+    RFError,
+    attn_decode,
+    attn_decode_partials,
+    attn_fwd,
+    absmax_quant_fp8,
+    absmax_quant_gemm_fp8,
+    lib,
+    merge_states,
+    rf_absmax_quant_fp8,
+    rf_absmax_quant_gemm_fp8,
+    rf_attn_decode_split,
+    rf_attn_fwd,
+    rf_merge_states,
+    rf_softmax_topk,
+    softmax_topk,
+)

@@ -1,0 +1,205 @@
+"""ctypes binding of ``librf.so``: argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+``include/rf.h``; this module only checks tensor shapes/dtypes/devices, takes
+raw device pointers and the current torch stream, and raises on a non-OK
+status. The ``rf_*`` functions have the C names and take caller-allocated
+output tensors; the short-named helpers allocate outputs with torch first.
+
+There is no fallback: if ``librf.so`` is missing, every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_LAUNCH = 0, 1, 2, 3
+RF_F32, RF_BF16 = 0, 1
+
+# Every entry point of the C ABI with its argument types.
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+SIGNATURES = {
+    "rf_attn_fwd": [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P],
+    "rf_attn_decode_split": [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
+    "rf_merge_states": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
+    "rf_softmax_topk": [_P, _I, _I, _I, _I, _P, _P, _P],
+    "rf_absmax_quant_fp8": [_P, _I, _I, _P, _P, _P],
+    "rf_absmax_quant_gemm_fp8": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
+    "rf_status_string": [_I],
+    "rf_last_error": [],
+    "rf_abi_version": [],
+}
+_RESTYPES = {"rf_status_string": ctypes.c_char_p, "rf_last_error": ctypes.c_char_p}
+
+_lib = None
+
+
+class RFError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{_status_name(status)}: {detail}")
+
+
+def _status_name(s):
+    return {0: "RF_OK", 1: "RF_ERR_INVALID_ARG", 2: "RF_ERR_UNSUPPORTED", 3: "RF_ERR_LAUNCH"}.get(s, str(s))
+
+
+def lib():
+    """Load librf.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() or "
+                "python -m online_softmax_attention_cascaded_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = _RESTYPES.get(name, ctypes.c_int)
+        _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status != RF_OK:
+        raise RFError(status, lib().rf_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("librf takes device tensors")
+        if not t.is_contiguous():
+            raise ValueError("librf takes contiguous tensors")
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return RF_F32
+    if t.dtype == torch.bfloat16:
+        return RF_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------- C-named calls
+
+
+def rf_attn_fwd(q, k, v, o, lse, scale, causal):
+    _dev(q, k, v, o, lse)
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    _check(lib().rf_attn_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                             B, Hq, Hkv, Lq, Lk, d, float(scale), int(bool(causal)), _stream(q)))
+
+
+def rf_attn_decode_split(q, k, v, part_m, part_l, part_acc, scale):
+    _dev(q, k, v, part_m, part_l, part_acc)
+    B, Hq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    S = part_m.shape[-1]
+    _check(lib().rf_attn_decode_split(_dtype_code(k), _ptr(q), _ptr(k), _ptr(v), _ptr(part_m),
+                                      _ptr(part_l), _ptr(part_acc), B, Hq, Hkv, Lk, d, S,
+                                      float(scale), _stream(q)))
+
+
+def rf_merge_states(part_m, part_l, part_acc, o, lse):
+    _dev(part_m, part_l, part_acc, o, lse)
+    S, d = part_acc.shape[-2], part_acc.shape[-1]
+    rows = part_m.numel() // S if S else 0
+    _check(lib().rf_merge_states(_ptr(part_m), _ptr(part_l), _ptr(part_acc), rows, S, d,
+                                 _dtype_code(o), _ptr(o), _ptr(lse), _stream(part_m)))
+
+
+def rf_softmax_topk(logits, k, renormalize, weights, indices):
+    _dev(logits, weights, indices)
+    T, E = logits.shape
+    _check(lib().rf_softmax_topk(_ptr(logits), T, E, int(k), int(bool(renormalize)), _ptr(weights),
+                                 _ptr(indices), _stream(logits)))
+
+
+def rf_absmax_quant_fp8(x, q, scale):
+    _dev(x, q, scale)
+    rows, cols = x.shape
+    _check(lib().rf_absmax_quant_fp8(_ptr(x), rows, cols, _ptr(q), _ptr(scale), _stream(x)))
+
+
+def rf_absmax_quant_gemm_fp8(a, b_q, b_scale, a_q, a_scale, c):
+    _dev(a, b_q, b_scale, a_q, a_scale, c)
+    M, K = a.shape
+    N = b_q.shape[0]
+    _check(lib().rf_absmax_quant_gemm_fp8(_ptr(a), _ptr(b_q), _ptr(b_scale), M, N, K, _ptr(a_q),
+                                          _ptr(a_scale), _ptr(c), _stream(a)))
+
+
+# ---------------------------------------------------------------- allocating helpers
+
+
+def attn_fwd(q, k, v, scale, causal=False, with_lse=True):
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if with_lse else None
+    rf_attn_fwd(q, k, v, o, lse, scale, causal)
+    return o, lse
+
+
+def attn_decode_partials(q, k, v, scale, S):
+    B, Hq, d = q.shape
+    part_m = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    part_l = torch.empty_like(part_m)
+    part_acc = torch.empty((B, Hq, S, d), dtype=torch.float32, device=q.device)
+    rf_attn_decode_split(q, k, v, part_m, part_l, part_acc, scale)
+    return part_m, part_l, part_acc
+
+
+def merge_states(part_m, part_l, part_acc, out_dtype=torch.bfloat16):
+    o = torch.empty(part_acc.shape[:-2] + part_acc.shape[-1:], dtype=out_dtype, device=part_acc.device)
+    lse = torch.empty(part_m.shape[:-1], dtype=torch.float32, device=part_m.device)
+    rf_merge_states(part_m, part_l, part_acc, o, lse)
+    return o, lse
+
+
+def attn_decode(q, k, v, scale, S, out_dtype=torch.bfloat16):
+    """Split-KV decode: partial states over S segments, then their merge."""
+    parts = attn_decode_partials(q, k, v, scale, S)
+    o, lse = merge_states(*parts, out_dtype=out_dtype)
+    return o, lse, parts
+
+
+def softmax_topk(logits, k, renormalize=True):
+    T = logits.shape[0]
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    rf_softmax_topk(logits, k, renormalize, w, idx)
+    return w, idx
+
+
+def absmax_quant_fp8(x):
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    rf_absmax_quant_fp8(x, q, s)
+    return q, s
+
+
+def absmax_quant_gemm_fp8(a, b_q, b_scale):
+    M, K = a.shape
+    N = b_q.shape[0]
+    a_q = torch.empty((M, K), dtype=torch.uint8, device=a.device)
+    a_scale = torch.empty(M, dtype=torch.float32, device=a.device)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    rf_absmax_quant_gemm_fp8(a, b_q, b_scale, a_q, a_scale, c)
+    return c, a_q, a_scale

@@ -1,0 +1,176 @@
+// C entry points of the library: argument validation, then one or two launches
+// on the caller's stream. Validation touches no HIP API, so every error return
+// happens before anything is enqueued (and works on a machine without a GPU).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/rf.h"
+#include "rf_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+rf_status fail(rf_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+rf_status ok() {
+  g_last_error[0] = '\0';
+  return RF_OK;
+}
+
+rf_status from_launch(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(RF_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define RF_REQUIRE(cond, status, ...)            \
+  do {                                           \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+rf_status rf_attn_fwd(rf_dtype dt, const void* q, const void* k, const void* v, void* o,
+                      float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale,
+                      int causal, hipStream_t stream) {
+  RF_REQUIRE(dt == RF_F32 || dt == RF_BF16, RF_ERR_INVALID_ARG, "rf_attn_fwd: unknown dtype %d", (int)dt);
+  RF_REQUIRE(B >= 0 && Hq >= 0 && Hkv >= 0 && Lq >= 0 && Lk >= 0 && d >= 0, RF_ERR_INVALID_ARG,
+             "rf_attn_fwd: negative size");
+  if ((long long)B * Hq * Lq == 0) return ok();
+  RF_REQUIRE(Hkv >= 1 && Hq % Hkv == 0, RF_ERR_INVALID_ARG, "rf_attn_fwd: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  RF_REQUIRE(Lk >= 1, RF_ERR_INVALID_ARG, "rf_attn_fwd: Lk must be >= 1");
+  RF_REQUIRE(!causal || Lq == Lk, RF_ERR_INVALID_ARG, "rf_attn_fwd: causal needs Lq == Lk (%d != %d)", Lq, Lk);
+  RF_REQUIRE(q && k && v && o, RF_ERR_INVALID_ARG, "rf_attn_fwd: null tensor pointer");
+  RF_REQUIRE(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(o, 16) && aligned(lse, 4),
+             RF_ERR_INVALID_ARG, "rf_attn_fwd: pointers must be 16-byte aligned");
+  RF_REQUIRE(scale == scale, RF_ERR_INVALID_ARG, "rf_attn_fwd: scale is NaN");
+  RF_REQUIRE((long long)B * Hq * (long long)(Lq > Lk ? Lq : Lk) * d < (1LL << 40), RF_ERR_INVALID_ARG,
+             "rf_attn_fwd: problem too large");
+  if (dt == RF_F32) {
+    RF_REQUIRE(d == 64 || d == 128, RF_ERR_UNSUPPORTED, "rf_attn_fwd: fp32 head size %d (need 64 or 128)", d);
+    return from_launch(rf::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                               static_cast<const float*>(v), static_cast<float*>(o), lse,
+                                               B, Hq, Hkv, Lq, Lk, d, scale, causal, stream),
+                       "rf_attn_fwd");
+  }
+  RF_REQUIRE(d == 128, RF_ERR_UNSUPPORTED, "rf_attn_fwd: bf16 head size %d (need 128)", d);
+  return from_launch(rf::launch_attn_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, scale, causal, stream),
+                     "rf_attn_fwd");
+}
+
+rf_status rf_attn_decode_split(rf_dtype dt, const void* q, const void* k, const void* v,
+                               float* part_m, float* part_l, float* part_acc, int B, int Hq,
+                               int Hkv, int Lk, int d, int S, float scale, hipStream_t stream) {
+  RF_REQUIRE(dt == RF_F32 || dt == RF_BF16, RF_ERR_INVALID_ARG, "rf_attn_decode_split: unknown dtype %d", (int)dt);
+  RF_REQUIRE(B >= 0 && Hq >= 0 && Hkv >= 0 && Lk >= 0 && d >= 0, RF_ERR_INVALID_ARG,
+             "rf_attn_decode_split: negative size");
+  RF_REQUIRE(S >= 1, RF_ERR_INVALID_ARG, "rf_attn_decode_split: S=%d must be >= 1", S);
+  if ((long long)B * Hq == 0) return ok();
+  RF_REQUIRE(Hkv >= 1 && Hq % Hkv == 0, RF_ERR_INVALID_ARG,
+             "rf_attn_decode_split: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  RF_REQUIRE(Lk >= 1, RF_ERR_INVALID_ARG, "rf_attn_decode_split: Lk must be >= 1");
+  RF_REQUIRE(q && k && v && part_m && part_l && part_acc, RF_ERR_INVALID_ARG,
+             "rf_attn_decode_split: null tensor pointer");
+  RF_REQUIRE(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(part_acc, 16) &&
+                 aligned(part_m, 4) && aligned(part_l, 4),
+             RF_ERR_INVALID_ARG, "rf_attn_decode_split: pointers must be 16-byte aligned");
+  RF_REQUIRE(scale == scale, RF_ERR_INVALID_ARG, "rf_attn_decode_split: scale is NaN");
+  RF_REQUIRE((long long)B * Hkv * Lk * d < (1LL << 40), RF_ERR_INVALID_ARG, "rf_attn_decode_split: problem too large");
+  RF_REQUIRE(dt == RF_BF16, RF_ERR_UNSUPPORTED, "rf_attn_decode_split: only bf16 K/V are supported");
+  RF_REQUIRE(d == 128, RF_ERR_UNSUPPORTED, "rf_attn_decode_split: head size %d (need 128)", d);
+  RF_REQUIRE(Hq / Hkv <= 16, RF_ERR_UNSUPPORTED, "rf_attn_decode_split: GQA group %d > 16", Hq / Hkv);
+  return from_launch(rf::launch_decode_split_bf16(q, k, v, part_m, part_l, part_acc, B, Hq, Hkv, Lk,
+                                                  d, S, scale, stream),
+                     "rf_attn_decode_split");
+}
+
+rf_status rf_merge_states(const float* part_m, const float* part_l, const float* part_acc,
+                          int rows, int S, int d, rf_dtype out_dt, void* o, float* lse,
+                          hipStream_t stream) {
+  RF_REQUIRE(out_dt == RF_F32 || out_dt == RF_BF16, RF_ERR_INVALID_ARG,
+             "rf_merge_states: unknown dtype %d", (int)out_dt);
+  RF_REQUIRE(rows >= 0 && d >= 0, RF_ERR_INVALID_ARG, "rf_merge_states: negative size");
+  RF_REQUIRE(S >= 1, RF_ERR_INVALID_ARG, "rf_merge_states: S=%d must be >= 1", S);
+  if (rows == 0) return ok();
+  RF_REQUIRE(d >= 1 && d <= 1024 && d % 4 == 0, RF_ERR_UNSUPPORTED,
+             "rf_merge_states: d=%d (need 4 <= d <= 1024, d %% 4 == 0)", d);
+  RF_REQUIRE(part_m && part_l && part_acc && o, RF_ERR_INVALID_ARG, "rf_merge_states: null tensor pointer");
+  RF_REQUIRE(aligned(part_acc, 16) && aligned(o, out_dt == RF_BF16 ? 8 : 16) && aligned(part_m, 4) &&
+                 aligned(part_l, 4) && aligned(lse, 4),
+             RF_ERR_INVALID_ARG, "rf_merge_states: misaligned pointer");
+  RF_REQUIRE((long long)rows * S * d < (1LL << 40), RF_ERR_INVALID_ARG, "rf_merge_states: problem too large");
+  return from_launch(rf::launch_merge_states(part_m, part_l, part_acc, rows, S, d, out_dt == RF_BF16, o,
+                                             lse, stream),
+                     "rf_merge_states");
+}
+
+rf_status rf_softmax_topk(const float* logits, int T, int E, int k, int renormalize,
+                          float* weights, int32_t* indices, hipStream_t stream) {
+  RF_REQUIRE(T >= 0 && E >= 0, RF_ERR_INVALID_ARG, "rf_softmax_topk: negative size");
+  RF_REQUIRE(E >= 1 && k >= 1 && k <= E, RF_ERR_INVALID_ARG, "rf_softmax_topk: need 1 <= k <= E (k=%d, E=%d)", k, E);
+  if (T == 0) return ok();
+  RF_REQUIRE(E <= 1024 && E % 4 == 0, RF_ERR_UNSUPPORTED, "rf_softmax_topk: E=%d (need E <= 1024, E %% 4 == 0)", E);
+  RF_REQUIRE(k <= 32, RF_ERR_UNSUPPORTED, "rf_softmax_topk: k=%d > 32", k);
+  RF_REQUIRE(logits && weights && indices, RF_ERR_INVALID_ARG, "rf_softmax_topk: null tensor pointer");
+  RF_REQUIRE(aligned(logits, 16) && aligned(weights, 4) && aligned(indices, 4), RF_ERR_INVALID_ARG,
+             "rf_softmax_topk: misaligned pointer");
+  return from_launch(rf::launch_softmax_topk(logits, T, E, k, renormalize != 0, weights, indices, stream),
+                     "rf_softmax_topk");
+}
+
+rf_status rf_absmax_quant_fp8(const void* x, int rows, int cols, uint8_t* q, float* scale,
+                              hipStream_t stream) {
+  RF_REQUIRE(rows >= 0 && cols >= 0, RF_ERR_INVALID_ARG, "rf_absmax_quant_fp8: negative size");
+  if (rows == 0) return ok();
+  RF_REQUIRE(cols >= 8 && cols % 8 == 0, RF_ERR_INVALID_ARG, "rf_absmax_quant_fp8: cols=%d must be a positive multiple of 8", cols);
+  RF_REQUIRE(cols <= 8192, RF_ERR_UNSUPPORTED, "rf_absmax_quant_fp8: cols=%d > 8192", cols);
+  RF_REQUIRE(x && q && scale, RF_ERR_INVALID_ARG, "rf_absmax_quant_fp8: null tensor pointer");
+  RF_REQUIRE(aligned(x, 16) && aligned(q, 8) && aligned(scale, 4), RF_ERR_INVALID_ARG,
+             "rf_absmax_quant_fp8: misaligned pointer");
+  return from_launch(rf::launch_absmax_quant_fp8(x, rows, cols, q, scale, stream), "rf_absmax_quant_fp8");
+}
+
+rf_status rf_absmax_quant_gemm_fp8(const void* a, const uint8_t* b, const float* b_scale, int M,
+                                   int N, int K, uint8_t* a_q, float* a_scale, void* c,
+                                   hipStream_t stream) {
+  RF_REQUIRE(M >= 0 && N >= 0 && K >= 0, RF_ERR_INVALID_ARG, "rf_absmax_quant_gemm_fp8: negative size");
+  if ((long long)M * N == 0) return ok();
+  RF_REQUIRE(K >= 128 && K % 128 == 0, RF_ERR_INVALID_ARG,
+             "rf_absmax_quant_gemm_fp8: K=%d must be a positive multiple of 128", K);
+  RF_REQUIRE(K <= 8192, RF_ERR_UNSUPPORTED, "rf_absmax_quant_gemm_fp8: K=%d > 8192", K);
+  RF_REQUIRE(a && b && b_scale && a_q && a_scale && c, RF_ERR_INVALID_ARG,
+             "rf_absmax_quant_gemm_fp8: null tensor pointer");
+  RF_REQUIRE(aligned(a, 16) && aligned(b, 16) && aligned(a_q, 16) && aligned(c, 4) &&
+                 aligned(b_scale, 4) && aligned(a_scale, 4),
+             RF_ERR_INVALID_ARG, "rf_absmax_quant_gemm_fp8: misaligned pointer");
+  hipError_t e = rf::launch_absmax_quant_fp8(a, M, K, a_q, a_scale, stream);
+  if (e != hipSuccess) return from_launch(e, "rf_absmax_quant_gemm_fp8 (quantise)");
+  return from_launch(rf::launch_gemm_fp8_scaled(a_q, a_scale, b, b_scale, M, N, K, c, stream),
+                     "rf_absmax_quant_gemm_fp8 (gemm)");
+}
+
+const char* rf_status_string(rf_status s) {
+  switch (s) {
+    case RF_OK: return "RF_OK";
+    case RF_ERR_INVALID_ARG: return "RF_ERR_INVALID_ARG";
+    case RF_ERR_UNSUPPORTED: return "RF_ERR_UNSUPPORTED";
+    case RF_ERR_LAUNCH: return "RF_ERR_LAUNCH";
+  }
+  return "unknown rf_status";
+}
+
+const char* rf_last_error(void) { return g_last_error; }
+
+int rf_abi_version(void) { return RF_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Device-side helpers shared by the gfx950 kernels: vector types for the MFMA
+// operands, bf16 / e4m3 conversions and wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rf {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// bf16 <-> fp32. A bf16 value is the upper half of an fp32 bit pattern, so the
+// widening is exact; the narrowing uses the hardware round-to-nearest-even
+// convert (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r.x = (__bf16)lo;
+  r.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Raw 2^x (v_exp_f32): exact enough for the softmax weights, no range fix-up;
+// 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- wavefront reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Merge of two online-softmax statistics (m, l): both rescaled to the larger max.
+// A side with m = -inf is the identity and contributes nothing.
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == kNegInf) return;
+  const float a = (m == kNegInf) ? 0.f : fast_exp2((m - mn) * kLog2e);
+  const float b = (m2 == kNegInf) ? 0.f : fast_exp2((m2 - mn) * kLog2e);
+  l = l * a + l2 * b;
+  m = mn;
+}
+
+// ---------------------------------------------------------------- e4m3 (OCP E4M3, no inf, max 448)
+
+// Round-to-nearest-even encoding of a finite fp32 value to an e4m3 code, with
+// the magnitude clamped to 448 first (saturation). Exact integer bit logic on
+// the fp32 pattern: subnormal codes hold m * 2^-9, normal codes hold
+// (1 + m/8) * 2^(e-7) with e in 1..15.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = __uint_as_float(bits & 0x7fffffffu);
+  uint32_t code;
+  if (a >= 448.f) {
+    code = 0x7eu;
+  } else if (a < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.f);  // 0..8; 8 is the smallest normal code
+  } else {
+    const uint32_t ab = bits & 0x7fffffffu;
+    const int e = (int)(ab >> 23) - 127;  // -6 .. 8
+    uint32_t mant = ab & 0x7fffffu;
+    uint32_t r = mant >> 20;
+    const uint32_t rem = mant & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+    int ee = e + 7;
+    if (r == 8u) { r = 0; ++ee; }
+    code = ((uint32_t)ee << 3) | r;
+    if (code > 0x7eu) code = 0x7eu;
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xfu, m = c & 7u;
+  float v = (e == 0) ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -v : v;
+}
+
+}  // namespace rf

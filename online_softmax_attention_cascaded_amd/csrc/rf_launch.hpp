@@ -1,0 +1,37 @@
+// Internal host-side launchers, one per kernel family. The C entry points in
+// rf_api.hip validate every argument first and then call these; each launcher
+// only enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rf {
+
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
+                               float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                               float scale, int causal, hipStream_t stream);
+
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale,
+                                int causal, hipStream_t stream);
+
+hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v, float* part_m,
+                                    float* part_l, float* part_acc, int B, int Hq, int Hkv, int Lk,
+                                    int d, int S, float scale, hipStream_t stream);
+
+hipError_t launch_merge_states(const float* part_m, const float* part_l, const float* part_acc,
+                               int rows, int S, int d, int out_bf16, void* o, float* lse,
+                               hipStream_t stream);
+
+hipError_t launch_softmax_topk(const float* logits, int T, int E, int k, int renormalize,
+                               float* weights, int32_t* indices, hipStream_t stream);
+
+hipError_t launch_absmax_quant_fp8(const void* x, int rows, int cols, uint8_t* q, float* scale,
+                                   hipStream_t stream);
+
+hipError_t launch_gemm_fp8_scaled(const uint8_t* a_q, const float* a_scale, const uint8_t* b_q,
+                                  const float* b_scale, int M, int N, int K, void* c,
+                                  hipStream_t stream);
+
+}  // namespace rf

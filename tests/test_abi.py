@@ -1,0 +1,160 @@
+"""The C ABI on the host (no GPU): the library loads, exports every entry point
+that include/rf.h declares, and rejects bad arguments before launching anything.
+Only argument combinations that fail validation are passed here, so no call
+reaches the HIP runtime."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from online_softmax_attention_cascaded_amd import binding
+from online_softmax_attention_cascaded_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rf.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+F32, BF16 = 0, 1
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        from online_softmax_attention_cascaded_amd import build
+
+        build.build()
+    return binding.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(rf_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    names = _declared()
+    assert names == sorted(binding.SIGNATURES), names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_argument_counts_match_header():
+    text = open(HEADER).read()
+    for name, args in binding.SIGNATURES.items():
+        m = re.search(r"\b" + name + r"\s*\(([^;]*?)\)\s*;", text, flags=re.S)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(args), (name, len(params), len(args))
+
+
+def test_status_helpers(lib):
+    assert lib.rf_abi_version() == 1
+    assert lib.rf_status_string(OK) == b"RF_OK"
+    assert lib.rf_status_string(INVALID) == b"RF_ERR_INVALID_ARG"
+    assert lib.rf_status_string(UNSUPPORTED) == b"RF_ERR_UNSUPPORTED"
+    assert lib.rf_status_string(3) == b"RF_ERR_LAUNCH"
+
+
+def attn(lib, dt=BF16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=2, Lq=64, Lk=64,
+         d=128, scale=0.1, causal=0):
+    return lib.rf_attn_fwd(dt, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, scale, causal, None)
+
+
+@pytest.mark.parametrize(
+    "kw,expect",
+    [
+        (dict(dt=7), INVALID),
+        (dict(B=-1), INVALID),
+        (dict(Hkv=3), INVALID),
+        (dict(Hkv=0), INVALID),
+        (dict(Lk=0), INVALID),
+        (dict(causal=1, Lk=32), INVALID),
+        (dict(q=None), INVALID),
+        (dict(o=MISALIGNED), INVALID),
+        (dict(scale=float("nan")), INVALID),
+        (dict(d=96), UNSUPPORTED),
+        (dict(dt=F32, d=96), UNSUPPORTED),
+        (dict(d=64), UNSUPPORTED),
+    ],
+)
+def test_attn_validation(lib, kw, expect):
+    assert attn(lib, **kw) == expect
+    assert lib.rf_last_error().startswith(b"rf_attn_fwd")
+
+
+def test_attn_empty_is_ok_without_pointers(lib):
+    assert attn(lib, q=None, k=None, v=None, o=None, B=0) == OK
+    assert attn(lib, q=None, k=None, v=None, o=None, Lq=0) == OK
+    assert lib.rf_last_error() == b""
+
+
+def decode(lib, dt=BF16, q=FAKE, k=FAKE, v=FAKE, m=FAKE, l=FAKE, acc=FAKE, B=1, Hq=8, Hkv=2,
+           Lk=100, d=128, S=4, scale=0.1):
+    return lib.rf_attn_decode_split(dt, q, k, v, m, l, acc, B, Hq, Hkv, Lk, d, S, scale, None)
+
+
+@pytest.mark.parametrize(
+    "kw,expect",
+    [
+        (dict(S=0), INVALID),
+        (dict(Hkv=3), INVALID),
+        (dict(Lk=0), INVALID),
+        (dict(acc=None), INVALID),
+        (dict(k=MISALIGNED), INVALID),
+        (dict(dt=F32), UNSUPPORTED),
+        (dict(d=64), UNSUPPORTED),
+        (dict(Hq=34, Hkv=2), UNSUPPORTED),
+    ],
+)
+def test_decode_validation(lib, kw, expect):
+    assert decode(lib, **kw) == expect
+
+
+def test_merge_validation(lib):
+    f = lib.rf_merge_states
+    assert f(FAKE, FAKE, FAKE, 4, 0, 128, BF16, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, -1, 2, 128, BF16, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 4, 2, 130, BF16, FAKE, None, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 4, 2, 2048, BF16, FAKE, None, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, None, 4, 2, 128, BF16, FAKE, None, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 4, 2, 128, 5, FAKE, None, None) == INVALID
+    assert f(None, None, None, 0, 2, 128, BF16, None, None, None) == OK
+
+
+def test_topk_validation(lib):
+    f = lib.rf_softmax_topk
+    assert f(FAKE, 10, 256, 0, 1, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 10, 8, 9, 1, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 10, 2048, 8, 1, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 10, 254, 8, 1, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 10, 256, 40, 1, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(MISALIGNED, 10, 256, 8, 1, FAKE, FAKE, None) == INVALID
+    assert f(None, 0, 256, 8, 1, None, None, None) == OK
+
+
+def test_quant_validation(lib):
+    f = lib.rf_absmax_quant_fp8
+    assert f(FAKE, 4, 12, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 4, 16384, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(None, 4, 64, FAKE, FAKE, None) == INVALID
+    assert f(None, 0, 64, None, None, None) == OK
+    g = lib.rf_absmax_quant_gemm_fp8
+    assert g(FAKE, FAKE, FAKE, 64, 64, 100, FAKE, FAKE, FAKE, None) == INVALID
+    assert g(FAKE, FAKE, FAKE, 64, 64, 16384, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert g(FAKE, FAKE, FAKE, 64, 64, 256, None, FAKE, FAKE, None) == INVALID
+    assert g(None, None, None, 0, 64, 256, None, None, None, None) == OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    x = torch.zeros(4, 256)
+    with pytest.raises(ValueError):
+        binding.softmax_topk(x, 8)

@@ -1,0 +1,50 @@
+"""GPU parity of rf_softmax_topk (through the C ABI) against the fp64 oracle:
+indices bit-exact (ties to the lower index), weights within 1e-5 relative."""
+
+import numpy as np
+import pytest
+
+import oracle
+import online_softmax_attention_cascaded_amd as rf
+from online_softmax_attention_cascaded_amd import inputs
+from gpu_util import DEV, needs_gpu, np32, print_case
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _check(x, k, renormalize):
+    w, idx = rf.softmax_topk(x.to(DEV), k, renormalize)
+    w_ref, idx_ref = oracle.softmax_topk(x.numpy(), k, renormalize)
+    got = idx.cpu().numpy()
+    bad = np.argwhere(got != idx_ref)
+    assert len(bad) == 0, f"first index mismatch at {bad[:3].tolist()}"
+    rel = np.abs(np32(w) - w_ref) / w_ref
+    assert rel.max() <= 1e-5, rel.max()
+
+
+@pytest.mark.parametrize("renormalize", [True, False])
+def test_routing_config(renormalize):
+    """16384 tokens x 256 experts, 1 % spiked rows, top-8."""
+    print_case(test="routing_full", renormalize=renormalize)
+    _check(inputs.routing_inputs(3, 16384, 256), 8, renormalize)
+
+
+@pytest.mark.parametrize("E,k", [(4, 1), (4, 4), (64, 2), (128, 8), (256, 32), (512, 8), (1024, 16), (1000, 5)])
+def test_routing_shapes(E, k):
+    print_case(test="routing_shapes", E=E, k=k)
+    _check(inputs.routing_inputs(9, 37, E), k, True)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_routing_ties(seed):
+    """Logits drawn from four values: almost every selection is a tie."""
+    _check(inputs.tie_heavy_logits(seed, 300, 256), 8, True)
+    _check(inputs.tie_heavy_logits(seed, 300, 64), 8, False)
+
+
+def test_routing_empty():
+    import torch
+
+    x = torch.zeros((0, 256), device=DEV)
+    w, idx = rf.softmax_topk(x, 8)
+    assert w.shape == (0, 8) and idx.shape == (0, 8)
