@@ -1,0 +1,324 @@
+"""Benchmark of the fused cascaded-reduction hot path on one MI355X.
+
+One step = one pass of every kernel of the path over one batch of synthetic,
+seeded input already resident in HBM:
+  prefill attention, bf16, B=4 H=32 L=2048 d=128, non-causal and causal;
+  split-KV decode, bf16 KV cache, B=8 Hq=32 Hkv=8 Lk=32768 d=128, S segments,
+    partial states + merge;
+  MoE routing, 16384 x 256 fp32 logits, softmax -> top-8 (renormalised);
+  FP8 per-token quantise + GEMM, M=N=4096, K=7168.
+Routing logits rotate over 20 buffers and the FP8 A operand over 5, so those
+inputs (which would otherwise fit the 256 MB last-level cache) come from HBM.
+
+Prints ONE JSON line. ``value`` is the mean of two fractions of MI355X peak:
+prefill (non-causal) TFLOP/s over the 2.5 PFLOP/s dense bf16 MFMA peak, and
+split-KV decode GB/s over the 8 TB/s HBM peak (best of the timed segment
+counts). Kernel times come from HIP events on the stream the kernels run on.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+PREFILL = dict(B=4, H=32, L=2048, d=128)
+DECODE = dict(B=8, Hq=32, Hkv=8, Lk=32768, d=128)
+ROUTING = dict(T=16384, E=256, k=8)
+FP8 = dict(M=4096, N=4096, K=7168)
+DECODE_SEGMENTS = (4, 16, 64)
+ROUTING_ROTATE = 20
+FP8_ROTATE = 5
+
+
+def prefill_flops(causal):
+    B, H, L, d = PREFILL["B"], PREFILL["H"], PREFILL["L"], PREFILL["d"]
+    pairs = L * (L + 1) // 2 if causal else L * L
+    return 4.0 * B * H * pairs * d
+
+
+def decode_bytes():
+    B, Hq, Hkv, Lk, d = (DECODE[x] for x in ("B", "Hq", "Hkv", "Lk", "d"))
+    return 2 * B * Hkv * Lk * d * 2 + 2 * B * Hq * d * 2   # K + V read, q read + O written
+
+
+def routing_bytes():
+    T, E, k = ROUTING["T"], ROUTING["E"], ROUTING["k"]
+    return T * E * 4 + T * k * 8
+
+
+def quant_bytes():
+    M, K = FP8["M"], FP8["K"]
+    return M * K * 2 + M * K + M * 4
+
+
+def gemm_flops():
+    return 2.0 * FP8["M"] * FP8["N"] * FP8["K"]
+
+
+def read_traffic():
+    """Measured HBM traffic per launch from profiles/traffic.txt, kept only while
+    the kernel source it was measured on is unchanged (matching hash)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        parts = line.split()
+        if len(parts) != 4 or line.startswith("#"):
+            continue
+        kernel, src, digest, nbytes = parts
+        src_path = os.path.join(ROOT, src)
+        if not os.path.exists(src_path):
+            continue
+        now = hashlib.sha256(open(src_path, "rb").read()).hexdigest()[:16]
+        if now == digest:
+            out[kernel] = float(nbytes)
+    return out
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands, timed on this host on a bounded sample of the same
+    workloads: whole (batch, head) slices of the non-causal prefill and whole
+    query rows of the S=16 decode, each run until about half the budget is spent."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from online_softmax_attention_cascaded_amd import inputs
+
+    P = PREFILL
+    q, k, v = inputs.attention_inputs(1, 1, 2, 2, P["L"], P["L"], P["d"])
+    scale = 1 / math.sqrt(P["d"])
+    n_heads, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s / 2 or n_heads == 0:
+        h = n_heads % 2
+        oracle.attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], scale)
+        n_heads += 1
+    t_pre = time.perf_counter() - t0
+    pre_tflops = n_heads * 4.0 * P["L"] * P["L"] * P["d"] / t_pre / 1e12
+
+    Dc = DECODE
+    qd, kd, vd = inputs.decode_inputs(2, 1, 4, 1, Dc["Lk"], Dc["d"])
+    n_rows, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s / 2 or n_rows == 0:
+        m, l, acc = oracle.decode_partials(qd, kd, vd, scale, 16)
+        oracle.merge_states(m, l, acc)
+        n_rows += qd.shape[1]
+    t_dec = time.perf_counter() - t0
+    # Bytes of the full workload per query row: its share of K/V (one GQA group of 4
+    # rows reads one K/V head) plus q and O.
+    bytes_per_row = (2 * Dc["Lk"] * Dc["d"] * 2) / (Dc["Hq"] // Dc["Hkv"]) + 2 * Dc["d"] * 2
+    dec_gbs = n_rows * bytes_per_row / t_dec / 1e9
+
+    blas = [i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    value = 0.5 * (pre_tflops / PEAK_BF16_TFLOPS + dec_gbs / PEAK_HBM_GBS) * 100
+    return {
+        "value": value,
+        "unit": "% of MI355X peak (mean of prefill/bf16-MFMA and decode/HBM fractions)",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: {n_heads} (batch, head) slices of the non-causal prefill "
+                   f"(L=2048, d=128) in {t_pre:.1f} s and {n_rows} query rows of the S=16 decode "
+                   f"(Lk=32768) in {t_dec:.1f} s; BLAS threads {cores}, numpy elementwise single-threaded"),
+        "prefill_tflops": pre_tflops,
+        "decode_gbs": dec_gbs,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one elementwise copy of 512 MiB first (reference kernel of known "
+                         "traffic for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU variant "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import online_softmax_attention_cascaded_amd as rf
+    from online_softmax_attention_cascaded_amd import inputs
+    from online_softmax_attention_cascaded_amd.build import LIB_PATH
+
+    if not os.path.exists(LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        progress("copy calibration kernel done (reads 512 MiB, writes 512 MiB)")
+
+    # ---------------- inputs (seeded, generated on the host, copied to HBM once)
+    progress("generating inputs")
+    P, Dc, R, F = PREFILL, DECODE, ROUTING, FP8
+    q, k, v = (t.to(dev) for t in inputs.attention_inputs(1, P["B"], P["H"], P["H"], P["L"], P["L"], P["d"]))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    scale = 1 / math.sqrt(P["d"])
+
+    qd, kd, vd = (t.to(dev) for t in inputs.decode_inputs(2, Dc["B"], Dc["Hq"], Dc["Hkv"], Dc["Lk"], Dc["d"]))
+    dec_bufs = {}
+    for S in DECODE_SEGMENTS:
+        dec_bufs[S] = (torch.empty((Dc["B"], Dc["Hq"], S), device=dev),
+                       torch.empty((Dc["B"], Dc["Hq"], S), device=dev),
+                       torch.empty((Dc["B"], Dc["Hq"], S, Dc["d"]), device=dev))
+    od = torch.empty((Dc["B"], Dc["Hq"], Dc["d"]), dtype=torch.bfloat16, device=dev)
+    lsed = torch.empty((Dc["B"], Dc["Hq"]), device=dev)
+
+    logits0 = inputs.routing_inputs(3, R["T"], R["E"]).to(dev)
+    logits = [logits0] + [logits0.clone() for _ in range(ROUTING_ROTATE - 1)]
+    rw = torch.empty((R["T"], R["k"]), device=dev)
+    ri = torch.empty((R["T"], R["k"]), dtype=torch.int32, device=dev)
+
+    a0, bsrc = inputs.quant_inputs(4, F["M"], F["N"], F["K"])
+    a_bufs = [a0.to(dev)] + [a0.to(dev) for _ in range(FP8_ROTATE - 1)]
+    bq, bs = rf.absmax_quant_fp8(bsrc.to(dev))
+    aq = torch.empty((F["M"], F["K"]), dtype=torch.uint8, device=dev)
+    sa = torch.empty(F["M"], device=dev)
+    c = torch.empty((F["M"], F["N"]), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    # ---------------- one step of the path, each kernel bracketed by events
+    names = ["prefill", "prefill_causal"] + [f"decode_s{S}" for S in DECODE_SEGMENTS] + ["routing", "fp8"]
+    times = {n: 0.0 for n in names}
+
+    def step(i, record):
+        ev = []
+
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                ev.append(e)
+
+        mark()
+        rf.rf_attn_fwd(q, k, v, o, lse, scale, False)
+        mark()
+        rf.rf_attn_fwd(q, k, v, o, lse, scale, True)
+        mark()
+        for S in DECODE_SEGMENTS:
+            pm, pl, pa = dec_bufs[S]
+            rf.rf_attn_decode_split(qd, kd, vd, pm, pl, pa, scale)
+            rf.rf_merge_states(pm, pl, pa, od, lsed)
+            mark()
+        rf.rf_softmax_topk(logits[i % ROUTING_ROTATE], R["k"], True, rw, ri)
+        mark()
+        rf.rf_absmax_quant_gemm_fp8(a_bufs[i % FP8_ROTATE], bq, bs, aq, sa, c)
+        mark()
+        return ev
+
+    progress("warmup")
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        events.append(step(i, True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for ev in events:
+        for n, a, b in zip(names, ev[:-1], ev[1:]):
+            times[n] += a.elapsed_time(b) / 1e3  # seconds
+    per = {n: times[n] / args.steps for n in names}  # seconds per launch group
+
+    pre_tflops = prefill_flops(False) / per["prefill"] / 1e12
+    pre_c_tflops = prefill_flops(True) / per["prefill_causal"] / 1e12
+    dec = {S: decode_bytes() / per[f"decode_s{S}"] / 1e9 for S in DECODE_SEGMENTS}
+    best_S = max(dec, key=dec.get)
+    dec_gbs = dec[best_S]
+    rout_gbs = routing_bytes() / per["routing"] / 1e9
+    pre_frac = pre_tflops / PEAK_BF16_TFLOPS
+    dec_frac = dec_gbs / PEAK_HBM_GBS
+    value = 0.5 * (pre_frac + dec_frac) * 100
+
+    traffic = read_traffic()
+    step_ms = wall / args.steps * 1e3
+    result = {
+        "metric": "prefill attn TFLOP/s + split-KV decode GB/s, as % of MI355X peak",
+        "value": round(value, 3),
+        "unit": "% of peak (mean of prefill bf16-MFMA fraction and decode HBM fraction)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1); routing spikes and FP8 outliers as configured)",
+        "config": {
+            "workload": "prefill attention B4 H32 L2048 d128 bf16 (non-causal and causal) + "
+                        "split-KV decode B8 Hq32 Hkv8 Lk32768 d128 bf16 + routing 16384x256 top-8 + "
+                        "FP8 quant+GEMM 4096x4096x7168",
+            "prefill": PREFILL, "decode": dict(DECODE, segments=list(DECODE_SEGMENTS)),
+            "routing": ROUTING, "fp8": FP8, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_bf16 (non-causal prefill)",
+            "achieved": round(pre_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pre_frac, 4),
+            "traffic": traffic.get("attn_fwd_bf16"),
+        },
+        "rooflines": {
+            "prefill_causal": {"bound": "mfma", "achieved": round(pre_c_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(pre_c_tflops / PEAK_BF16_TFLOPS, 4)},
+            "decode": {"bound": "hbm", "segments": best_S, "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                       "unit": "GB/s", "frac": round(dec_frac, 4),
+                       "by_segments": {str(S): round(x, 1) for S, x in dec.items()},
+                       "traffic": traffic.get("decode_split")},
+            "routing": {"bound": "hbm", "achieved": round(rout_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(rout_gbs / PEAK_HBM_GBS, 4)},
+            "fp8_quant_gemm": {"bound": "mfma", "achieved": round(gemm_flops() / per["fp8"] / 1e12, 2),
+                               "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(gemm_flops() / per["fp8"] / 1e12 / PEAK_FP8_TFLOPS, 4),
+                               "note": "quantiser + GEMM time, GEMM flops only"},
+        },
+        "us_per_launch": {n: round(per[n] * 1e6, 2) for n in names},
+        "tokens_per_s": {
+            "prefill": PREFILL["B"] * PREFILL["L"] / per["prefill"],
+            "decode": DECODE["B"] / per[f"decode_s{best_S}"],
+            "routing": ROUTING["T"] / per["routing"],
+            "fp8": FP8["M"] / per["fp8"],
+        },
+    }
+    progress(f"timed {args.steps} steps in {wall:.2f} s")
+    if not args.no_cpu_baseline:
+        progress("timing the oracle on the host")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
