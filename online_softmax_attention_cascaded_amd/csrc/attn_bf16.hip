@@ -1,10 +1,10 @@
 // bf16 attention forward for head size 128 on gfx950 MFMA.
 //
 // One pass over 64-key tiles of K and V per block of 128 query rows, with a
-// running max m, running denominator l and an fp32 accumulator per row; when a
-// tile raises the max the state is rescaled by exp(m_old - m_new), and the
-// accumulator is divided by l once at the end ("RedFuser episode transcript",
-// cues 15-19). Both contractions run on v_mfma_f32_32x32x16_bf16.
+// running reference max m, running denominator l and an fp32 accumulator per
+// row; when the reference moves the state is rescaled by exp(m_old - m_new),
+// and the accumulator is divided by l once at the end ("RedFuser episode
+// transcript", cues 15-19). Both contractions run on v_mfma_f32_32x32x16_bf16.
 //
 // Layout choices (CDNA4, wave64):
 //  * Scores are computed transposed, S^T = K Q^T, so each lane owns ONE query
@@ -12,12 +12,19 @@
 //    rescale of the output are then lane-local, and the probabilities already
 //    sit in the B-operand layout of the second product O^T = V^T P^T.
 //  * The second product needs V with keys contiguous per lane, so V tiles are
-//    written into LDS transposed (Vt[d][key]). Keys are stored in the order the
+//    written into LDS transposed (Vt[d][key]); keys are stored in the order the
 //    MFMA k-slots expect (bits 2 and 3 of the key index swapped), so each lane
 //    reads its 8 keys with one 16-byte LDS read.
-//  * K tiles stay row-major in LDS with the 16-byte chunk index XOR-swizzled by
-//    the row, and Vt rows are swizzled the same way, so the 16-byte operand
-//    reads of consecutive lanes fall in distinct banks.
+//  * LDS rows are XOR-swizzled (K: chunk ^ (row & 15) on 256-byte rows; Vt:
+//    chunk ^ ((d ^ d >> 3) & 7) on 128-byte rows), so the 16-byte operand reads
+//    of consecutive lanes, and the transposing 8-byte writes, spread over the
+//    banks. All LDS addresses are loop-invariant registers plus immediate
+//    offsets; the loop is unrolled by two so the double-buffer offset is an
+//    immediate too.
+//  * The reference max is moved only when a score exceeds it by more than 2^8
+//    (in exp2 units), which is rare after the first tile; l and the accumulator
+//    always share the same reference, so O = acc / l and lse = m + ln l are
+//    exact whatever the reference.
 //  * Tiles are double-buffered in LDS: the global loads of tile t+1 are issued
 //    before tile t is computed and written to the other buffer afterwards.
 //  * Workgroups of one (batch, head) are placed on the same XCD (workgroups are
@@ -34,14 +41,8 @@ constexpr int BM = 128;  // query rows per workgroup, 32 per wave
 constexpr int BN = 64;   // keys per tile
 constexpr int kKBytes = BN * D * 2;
 constexpr int kStage = 2 * kKBytes;  // K tile + transposed V tile
+constexpr float kTau = 8.f;          // lazy-rescale threshold, exp2 units
 
-__device__ __forceinline__ int k_off(int row, int chunk) {
-  return row * 256 + ((chunk ^ (row & 15)) << 4);
-}
-__device__ __forceinline__ int vt_off(int d, int pos) {
-  const int swz = (d ^ (d >> 3)) & 7;
-  return d * 128 + (((pos >> 3) ^ swz) << 4) + ((pos >> 2) & 1) * 8;
-}
 // Position of key k (0..63) inside a transposed V row: bits 2 and 3 swapped.
 __device__ __forceinline__ int key_pos(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
@@ -49,6 +50,10 @@ __device__ __forceinline__ int key_pos(int k) {
 
 __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
 template <bool CAUSAL>
@@ -94,121 +99,152 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
   const int ntiles = (kend + BN - 1) / BN;
 
-  // Global -> register staging of one tile.
-  const int lc = tid & 15;    // 16-byte chunk of a 256-byte row
-  const int lr = tid >> 4;    // K: row lr + 16*i ; V: keys 4*lr + j
+  // ---- global -> register staging of one tile (thread: 16-byte chunk lc of
+  // K rows lr + 16 i, and of V keys 4 lr + j). Buffer loads: rows past Lk read 0
+  // (they are masked out of the scores).
+  const int lc = tid & 15, lr = tid >> 4;
+  const uint32_t kv_bytes = (uint32_t)Lk * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, kv_bytes);
+  const int kvo = (lr * D + 8 * lc) * 2;
+  const int vvo = (4 * lr * D + 8 * lc) * 2;
   u32x4 kreg[4], vreg[4];
   auto load_tile = [&](int t) {
-    const int t0 = t * BN;
+    const int tb = t * BN * D * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(t0 + lr + 16 * i, Lk - 1);
-      kreg[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)key * D + 8 * lc);
-    }
+    for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(krs, kvo, tb + i * 16 * D * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = min(t0 + 4 * lr + j, Lk - 1);
-      vreg[j] = *reinterpret_cast<const u32x4*>(vp + (size_t)key * D + 8 * lc);
-    }
+    for (int j = 0; j < 4; ++j) vreg[j] = buf_load16(vrs, vvo, tb + j * D * 2);
   };
-  auto store_tile = [&](int buf) {
-    char* kb = smem + buf * kStage;
-    char* vb = kb + kKBytes;
+
+  // ---- lane-constant LDS offsets.
+  // K write: row lr + 16 i, chunk lc ^ (row & 15) = lc ^ lr.
+  const int kw = lr * 256 + ((lc ^ lr) << 4);
+  // Vt write: rows d = 8 lc + jj (jj = 2e + hh), position key_pos(4 lr); the
+  // chunk is swizzled by vt_swz(d) = (d ^ (d >> 3)) & 7, which differs across
+  // the 8 values of lc that write the same jj together.
+  const int vpos = key_pos(4 * lr);
+  const int vch = vpos >> 3;
+  const int vw = kKBytes + 8 * lc * 128 + ((vpos >> 2) & 1) * 8;
+  int vwj[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(kb + k_off(lr + 16 * i, lc)) = kreg[i];
-    const int pos = key_pos(4 * lr);
+  for (int jj = 0; jj < 8; ++jj) vwj[jj] = vw + jj * 128 + ((vch ^ ((jj ^ lc) & 7)) << 4);
+  // K read (A operand): row li (+32 kb), chunk (2 ds + g) ^ (li & 15).
+  int kr[8];
+#pragma unroll
+  for (int ds = 0; ds < 8; ++ds) kr[ds] = li * 256 + (((2 * ds + g) ^ (li & 15)) << 4);
+  // Vt read (A operand of O^T = V^T P^T): row d = 32 db + li, chunk (2 ks + g) ^ vt_swz(d).
+  int vr[4][4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = 32 * db + li, swz = (d ^ (d >> 3)) & 7;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) vr[db][ks] = kKBytes + d * 128 + (((2 * ks + g) ^ swz) << 4);
+  }
+
+  auto store_tile = [&](char* buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(buf + kw + i * 16 * 256) = kreg[i];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t a0 = vreg[0][e], a1 = vreg[1][e], a2 = vreg[2][e], a3 = vreg[3][e];
-      const int d = 8 * lc + 2 * e;
       u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
       u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-      *reinterpret_cast<u32x2*>(vb + vt_off(d, pos)) = lo;
-      *reinterpret_cast<u32x2*>(vb + vt_off(d + 1, pos)) = hi;
+      *reinterpret_cast<u32x2*>(buf + vwj[2 * e]) = lo;
+      *reinterpret_cast<u32x2*>(buf + vwj[2 * e + 1]) = hi;
     }
   };
 
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-  float m_run = kNegInf;  // running max of the raw dot products of row qrow
-  float l_run = 0.f;      // running denominator relative to m_run * c (log2 units)
+  float m_c = kNegInf;  // reference max of row qrow, in exp2 units (score * c)
+  float l_run = 0.f;    // running denominator relative to m_c
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load_tile(t + 1);
+  auto compute = [&](const char* buf, int t) {
     const int t0 = t * BN;
-    const bool active = !CAUSAL || t0 <= wave_last_row;
-    if (active) {
-      const char* kb = smem + (t & 1) * kStage;
-      const char* vb = kb + kKBytes;
-      // ---- S^T = K Q^T for the tile's two 32-key blocks.
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+    // ---- S^T = K Q^T for the tile's two 32-key blocks.
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-      for (int ds = 0; ds < 8; ++ds) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + k_off(li, 2 * ds + g));
-        const bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(kb + k_off(32 + li, 2 * ds + g));
-        s0 = mfma_bf16(ka, qf[ds], s0);
-        s1 = mfma_bf16(kb1, qf[ds], s1);
-      }
-      // ---- mask: keys past Lk, and keys after the row when causal.
-      const bool need_mask = (t0 + BN > Lk) || (CAUSAL && t0 + BN - 1 > q0 + wave * 32);
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key0 = t0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const int key1 = key0 + 32;
-          if (key0 >= Lk || (CAUSAL && key0 > qrow)) s0[r] = kNegInf;
-          if (key1 >= Lk || (CAUSAL && key1 > qrow)) s1[r] = kNegInf;
-        }
-      }
-      // ---- online statistics of row qrow (its 64 scores are split over lanes li, li+32).
-      float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run, mx);
-      const float mc = (m_new == kNegInf) ? 0.f : m_new * c;
-      const float alpha = fast_exp2(m_run * c - mc);  // 0 while m_run = -inf
-      float rs = 0.f;
+    for (int ds = 0; ds < 8; ++ds) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(buf + kr[ds]);
+      const bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(buf + kr[ds] + 32 * 256);
+      s0 = mfma_bf16(ka, qf[ds], s0);
+      s1 = mfma_bf16(kb1, qf[ds], s1);
+    }
+    // ---- mask: keys past Lk, and keys after the row when causal.
+    const bool need_mask = (t0 + BN > Lk) || (CAUSAL && t0 + BN - 1 > q0 + wave * 32);
+    if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s0[r] = fast_exp2(fmaf(s0[r], c, -mc));
-        s1[r] = fast_exp2(fmaf(s1[r], c, -mc));
-        rs += s0[r] + s1[r];
-      }
-      rs += __shfl_xor(rs, 32, kWave);
-      l_run = alpha * l_run + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-      // ---- P^T (bf16) in the B-operand layout: k-step ks uses registers 8*(ks&1) .. +7.
-      bf16x8 pf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const f32x16& src = (ks < 2) ? s0 : s1;
-        const int base = 8 * (ks & 1);
-        bf16x8 p;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = (__bf16)src[base + j];
-        pf[ks] = p;
-      }
-      // ---- O^T += V^T P^T.
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 va =
-              *reinterpret_cast<const bf16x8*>(vb + vt_off(32 * db + li, 16 * ks + 8 * g));
-          oacc[db] = mfma_bf16(va, pf[ks], oacc[db]);
-        }
+        const int key0 = t0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int key1 = key0 + 32;
+        if (key0 >= Lk || (CAUSAL && key0 > qrow)) s0[r] = kNegInf;
+        if (key1 >= Lk || (CAUSAL && key1 > qrow)) s1[r] = kNegInf;
       }
     }
-    if (t + 1 < ntiles) store_tile((t + 1) & 1);
+    // ---- tile max of row qrow (its 64 scores are split over lanes li, li+32).
+    float mx = __builtin_fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mxc = mx * c;
+    if (t == 0) {
+      m_c = mxc;  // every row sees key 0, so this is finite
+    } else if (__any(mxc > m_c + kTau)) {
+      float alpha = 1.f;
+      if (mxc > m_c + kTau) {
+        alpha = fast_exp2(m_c - mxc);
+        m_c = mxc;
+      }
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    }
+    // ---- P^T (bf16) in the B-operand layout: k-step ks uses registers 8*(ks&1) .. +7
+    // of s0 (ks < 2) or s1; the row sum stays in fp32 so lse keeps fp32 accuracy.
+    bf16x8 pf[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const f32x16& src = (ks < 2) ? s0 : s1;
+      const int base = 8 * (ks & 1);
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(fmaf(src[base + 2 * j], c, -m_c));
+        const float p1 = fast_exp2(fmaf(src[base + 2 * j + 1], c, -m_c));
+        rs += p0 + p1;
+        w[j] = pack_bf16x2(p0, p1);
+      }
+      pf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+    rs += __shfl_xor(rs, 32, kWave);
+    l_run += rs;
+    // ---- O^T += V^T P^T.
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(buf + vr[db][ks]);
+        oacc[db] = mfma_bf16(va, pf[ks], oacc[db]);
+      }
+    }
+  };
+
+  auto step = [&](char* cur, char* nxt, int t) {
+    if (t + 1 < ntiles) load_tile(t + 1);
+    if (!CAUSAL || t * BN <= wave_last_row) compute(cur, t);
+    if (t + 1 < ntiles) store_tile(nxt);
     __syncthreads();
+  };
+
+  load_tile(0);
+  store_tile(smem);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(smem, smem + kStage, t);
+    if (t + 1 < ntiles) step(smem + kStage, smem, t + 1);
   }
 
   // ---- epilogue: O = acc / l (bf16), lse = m + ln l.
@@ -225,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
         *reinterpret_cast<u32x2*>(orow + d0) = w;
       }
     }
-    if (lse && g == 0) lse[(size_t)bh * Lq + qrow] = (m_run * c + __log2f(l_run)) * kLn2;
+    if (lse && g == 0) lse[(size_t)bh * Lq + qrow] = (m_c + __log2f(l_run)) * kLn2;
   }
 }
 
