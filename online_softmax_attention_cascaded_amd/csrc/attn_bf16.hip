@@ -6,27 +6,23 @@
 // and the accumulator is divided by l once at the end ("RedFuser episode
 // transcript", cues 15-19). Both contractions run on v_mfma_f32_32x32x16_bf16.
 //
-// Layout choices (CDNA4, wave64):
+// Layout and schedule (CDNA4, wave64):
 //  * Scores are computed transposed, S^T = K Q^T, so each lane owns ONE query
 //    row (lane & 31) and 32 of the tile's keys; the softmax statistics and the
-//    rescale of the output are then lane-local, and the probabilities already
-//    sit in the B-operand layout of the second product O^T = V^T P^T.
-//  * The second product needs V with keys contiguous per lane, so V tiles are
-//    written into LDS transposed (Vt[d][key]); keys are stored in the order the
-//    MFMA k-slots expect (bits 2 and 3 of the key index swapped), so each lane
-//    reads its 8 keys with one 16-byte LDS read.
-//  * LDS rows are XOR-swizzled (K: chunk ^ (row & 15) on 256-byte rows; Vt:
-//    chunk ^ ((d ^ d >> 3) & 7) on 128-byte rows), so the 16-byte operand reads
-//    of consecutive lanes, and the transposing 8-byte writes, spread over the
-//    banks. All LDS addresses are loop-invariant registers plus immediate
-//    offsets; the loop is unrolled by two so the double-buffer offset is an
-//    immediate too.
+//    rescale of the output are lane-local, and the probabilities already sit
+//    in the B-operand layout of the second product O^T = V^T P^T.
+//  * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
+//    flag: no staging registers, rows past the end read as 0), row-major with
+//    the 16-byte chunks XOR-swizzled by the row so operand reads spread over the
+//    banks. V^T operands are read with the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b16), four keys of one column per lane per read.
+//  * K runs one tile ahead of V: while the softmax of tile t runs on the VALU,
+//    the scores of tile t+1 are already being computed on the matrix cores.
+//    Two LDS buffers per operand; one barrier per tile.
 //  * The reference max is moved only when a score exceeds it by more than 2^8
 //    (in exp2 units), which is rare after the first tile; l and the accumulator
 //    always share the same reference, so O = acc / l and lse = m + ln l are
 //    exact whatever the reference.
-//  * Tiles are double-buffered in LDS: the global loads of tile t+1 are issued
-//    before tile t is computed and written to the other buffer afterwards.
 //  * Workgroups of one (batch, head) are placed on the same XCD (workgroups are
 //    dealt round-robin to the 8 XCDs), so its K/V stream is shared in one L2.
 //    Causal blocks are issued longest first.
@@ -37,16 +33,18 @@ namespace rf {
 namespace {
 
 constexpr int D = 128;
-constexpr int BM = 128;  // query rows per workgroup, 32 per wave
-constexpr int BN = 64;   // keys per tile
-constexpr int kKBytes = BN * D * 2;
-constexpr int kStage = 2 * kKBytes;  // K tile + transposed V tile
-constexpr float kTau = 8.f;          // lazy-rescale threshold, exp2 units
+constexpr int BM = 128;                 // query rows per workgroup, 32 per wave
+constexpr int BN = 64;                  // keys per tile
+constexpr int kTileBytes = BN * D * 2;  // 16 KB per operand tile
+constexpr float kTau = 8.f;             // lazy-rescale threshold, exp2 units
 
-// Position of key k (0..63) inside a transposed V row: bits 2 and 3 swapped.
-__device__ __forceinline__ int key_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+struct Scores {
+  f32x16 s0, s1;  // keys 0..31 and 32..63 of the tile (accumulator layout)
+};
 
 __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -56,12 +54,19 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
+// Four keys (rows) of one head-size column per lane, transposed from the
+// row-major tile by the LDS (see the read-address comment in the kernel).
+__device__ __forceinline__ s16x4 tr_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int BH,
     int Hq, int Hkv, int Lq, int Lk, float c, int nqb) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  // [K0 | K1 | V0 | V1], 16 KB each.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
 
   // Workgroup -> (batch*head, query block).
   const int id = blockIdx.x;
@@ -99,61 +104,53 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
   const int ntiles = (kend + BN - 1) / BN;
 
-  // ---- global -> register staging of one tile (thread: 16-byte chunk lc of
-  // K rows lr + 16 i, and of V keys 4 lr + j). Buffer loads: rows past Lk read 0
-  // (they are masked out of the scores).
-  const int lc = tid & 15, lr = tid >> 4;
+  // ---- HBM -> LDS. Each wave fills four 1 KB blocks (4 rows of 256 B) per
+  // tile; lane l writes 16 bytes at block + 16 l, i.e. row 16*wave + 4*i + l/16,
+  // physical chunk l%16, so it fetches the logical chunk that the swizzle puts
+  // there: K chunk = phys ^ (row & 15), V chunk = phys ^ 2*(row & 7).
   const uint32_t kv_bytes = (uint32_t)Lk * D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, kv_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, kv_bytes);
-  const int kvo = (lr * D + 8 * lc) * 2;
-  const int vvo = (4 * lr * D + 8 * lc) * 2;
-  u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](int t) {
-    const int tb = t * BN * D * 2;
+  int kso[4], vso[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(krs, kvo, tb + i * 16 * D * 2);
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * wave + 4 * i + (lane >> 4), pc = lane & 15;
+    kso[i] = row * 256 + ((pc ^ (row & 15)) << 4);
+    vso[i] = row * 256 + ((pc ^ (2 * (row & 7))) << 4);
+  }
+  auto load_k = [&](int t, char* buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vreg[j] = buf_load16(vrs, vvo, tb + j * D * 2);
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + (4 * wave + i) * 1024), 16,
+                                               kso[i], t * kTileBytes, 0, 0);
+  };
+  auto load_v = [&](int t, char* buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(buf + (4 * wave + i) * 1024), 16,
+                                               vso[i], t * kTileBytes, 0, 0);
   };
 
-  // ---- lane-constant LDS offsets.
-  // K write: row lr + 16 i, chunk lc ^ (row & 15) = lc ^ lr.
-  const int kw = lr * 256 + ((lc ^ lr) << 4);
-  // Vt write: rows d = 8 lc + jj (jj = 2e + hh), position key_pos(4 lr); the
-  // chunk is swizzled by vt_swz(d) = (d ^ (d >> 3)) & 7, which differs across
-  // the 8 values of lc that write the same jj together.
-  const int vpos = key_pos(4 * lr);
-  const int vch = vpos >> 3;
-  const int vw = kKBytes + 8 * lc * 128 + ((vpos >> 2) & 1) * 8;
-  int vwj[8];
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) vwj[jj] = vw + jj * 128 + ((vch ^ ((jj ^ lc) & 7)) << 4);
-  // K read (A operand): row li (+32 kb), chunk (2 ds + g) ^ (li & 15).
+  // ---- LDS -> registers.
+  // K (A operand of S^T): row li (+32 kb), logical chunk 2 ds + g.
   int kr[8];
 #pragma unroll
   for (int ds = 0; ds < 8; ++ds) kr[ds] = li * 256 + (((2 * ds + g) ^ (li & 15)) << 4);
-  // Vt read (A operand of O^T = V^T P^T): row d = 32 db + li, chunk (2 ks + g) ^ vt_swz(d).
-  int vr[4][4];
+  // V^T (A operand of O^T, lane = head-size column 32 db + li, k-slots 8 g..8 g+7).
+  // The MFMA k-slots of k-step ks are, for lane half g, the keys
+  // 16 ks + 4 g + {0..3} (slots 0..3) and 16 ks + 8 + 4 g + {0..3} (slots 4..7):
+  // the layout of the score accumulator rows. One transposing read gives lane
+  // i of a 16-lane group the four keys k0..k0+3 of column d0 + i, when lane j
+  // of the group points at row k0 + j/4, columns d0 + 4 (j%4) .. +3.
+  int vr[4];
+  {
+    const int j = lane & 15, G = (lane >> 4) & 1;
+    const int row = 4 * g + (j >> 2);       // + 16 ks + 8 hh (immediates)
+    const int x = 2 * (row & 7);            // swizzle of every row this lane reads
+    const int cl = 2 * G + ((j >> 1) & 1);  // chunk within the 32-column block
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int d = 32 * db + li, swz = (d ^ (d >> 3)) & 7;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) vr[db][ks] = kKBytes + d * 128 + (((2 * ks + g) ^ swz) << 4);
+    for (int db = 0; db < 4; ++db) vr[db] = row * 256 + (((4 * db + cl) ^ x) << 4) + 8 * (j & 1);
   }
-
-  auto store_tile = [&](char* buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(buf + kw + i * 16 * 256) = kreg[i];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t a0 = vreg[0][e], a1 = vreg[1][e], a2 = vreg[2][e], a3 = vreg[3][e];
-      u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-      u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-      *reinterpret_cast<u32x2*>(buf + vwj[2 * e]) = lo;
-      *reinterpret_cast<u32x2*>(buf + vwj[2 * e + 1]) = hi;
-    }
-  };
 
   f32x16 oacc[4];
 #pragma unroll
@@ -161,32 +158,43 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   float m_c = kNegInf;  // reference max of row qrow, in exp2 units (score * c)
   float l_run = 0.f;    // running denominator relative to m_c
 
-  auto compute = [&](const char* buf, int t) {
-    const int t0 = t * BN;
-    // ---- S^T = K Q^T for the tile's two 32-key blocks.
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+  char* const K0 = smem;
+  char* const K1 = smem + kTileBytes;
+  char* const V0 = smem + 2 * kTileBytes;
+  char* const V1 = smem + 3 * kTileBytes;
+  auto active = [&](int t) { return !CAUSAL || t * BN <= wave_last_row; };
+
+  // Scores of one tile: 8 k-steps on two independent accumulators.
+  auto scores = [&](const char* kb, Scores& s) {
+    s.s0 = f32x16{};
+    s.s1 = f32x16{};
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(buf + kr[ds]);
-      const bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(buf + kr[ds] + 32 * 256);
-      s0 = mfma_bf16(ka, qf[ds], s0);
-      s1 = mfma_bf16(kb1, qf[ds], s1);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + kr[ds]);
+      const bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(kb + kr[ds] + 32 * 256);
+      s.s0 = mfma_bf16(ka, qf[ds], s.s0);
+      s.s1 = mfma_bf16(kb1, qf[ds], s.s1);
     }
-    // ---- mask: keys past Lk, and keys after the row when causal.
+  };
+
+  // One tile: softmax of tile t (scores `cur`) and O += V(t) P(t), with the
+  // scores of tile t+1 computed into `nxt` in the same instruction stream so
+  // the matrix cores work while the exponentials run on the VALU.
+  auto tile = [&](int t, Scores& cur, Scores& nxt, const char* knext, const char* vb) {
+    const int t0 = t * BN;
     const bool need_mask = (t0 + BN > Lk) || (CAUSAL && t0 + BN - 1 > q0 + wave * 32);
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key0 = t0 + 8 * (r >> 2) + 4 * g + (r & 3);
         const int key1 = key0 + 32;
-        if (key0 >= Lk || (CAUSAL && key0 > qrow)) s0[r] = kNegInf;
-        if (key1 >= Lk || (CAUSAL && key1 > qrow)) s1[r] = kNegInf;
+        if (key0 >= Lk || (CAUSAL && key0 > qrow)) cur.s0[r] = kNegInf;
+        if (key1 >= Lk || (CAUSAL && key1 > qrow)) cur.s1[r] = kNegInf;
       }
     }
-    // ---- tile max of row qrow (its 64 scores are split over lanes li, li+32).
-    float mx = __builtin_fmaxf(s0[0], s1[0]);
+    float mx = __builtin_fmaxf(cur.s0[0], cur.s1[0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
+    for (int r = 1; r < 16; ++r) mx = max3(mx, cur.s0[r], cur.s1[r]);
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float mxc = mx * c;
     if (t == 0) {
@@ -201,50 +209,84 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
     }
-    // ---- P^T (bf16) in the B-operand layout: k-step ks uses registers 8*(ks&1) .. +7
-    // of s0 (ks < 2) or s1; the row sum stays in fp32 so lse keeps fp32 accuracy.
-    bf16x8 pf[4];
+    // ---- from here on one basic block, in a fixed issue order: MFMA i of the
+    // scores of tile t+1 (K fragment read three steps ahead), then the VALU work
+    // for probabilities 2i, 2i+1 of tile t (2 fma, 2 exp2, 1 bf16 pack, 2 adds);
+    // sched_barrier fences keep the compiler from regrouping them. Then the 16
+    // P V MFMAs, each with its two transposing V reads issued two MFMAs ahead.
+    nxt.s0 = f32x16{};
+    nxt.s1 = f32x16{};
+    bf16x8 kf[4];
+    auto kread = [&](int i) {
+      return *reinterpret_cast<const bf16x8*>(knext + kr[i >> 1] + (i & 1) * 32 * 256);
+    };
+    kf[0] = kread(0);
+    kf[1] = kread(1);
+    kf[2] = kread(2);
+    u32x4 pw[4];
     float rs = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f32x16& src = (ks < 2) ? s0 : s1;
-      const int base = 8 * (ks & 1);
-      u32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = fast_exp2(fmaf(src[base + 2 * j], c, -m_c));
-        const float p1 = fast_exp2(fmaf(src[base + 2 * j + 1], c, -m_c));
-        rs += p0 + p1;
-        w[j] = pack_bf16x2(p0, p1);
-      }
-      pf[ks] = __builtin_bit_cast(bf16x8, w);
+    for (int i = 0; i < 16; ++i) {
+      if (i + 3 < 16) kf[(i + 3) & 3] = kread(i + 3);
+      if (i & 1)
+        nxt.s1 = mfma_bf16(kf[i & 3], qf[i >> 1], nxt.s1);
+      else
+        nxt.s0 = mfma_bf16(kf[i & 3], qf[i >> 1], nxt.s0);
+      // probabilities 2i, 2i+1: k-step ks = i/4, pair jj = i%4 of P^T's B operand
+      const int ks = i >> 2, jj = i & 3;
+      const f32x16& src = (ks < 2) ? cur.s0 : cur.s1;
+      const int e = 8 * (ks & 1) + 2 * jj;
+      const float p0 = fast_exp2(fmaf(src[e], c, -m_c));
+      const float p1 = fast_exp2(fmaf(src[e + 1], c, -m_c));
+      rs += p0 + p1;
+      pw[ks][jj] = pack_bf16x2(p0, p1);
+      __builtin_amdgcn_sched_barrier(0);
     }
     rs += __shfl_xor(rs, 32, kWave);
     l_run += rs;
-    // ---- O^T += V^T P^T.
+    // O^T += V^T P^T; consecutive MFMAs update different accumulators.
+    bf16x8 vf[3];
+    auto vread = [&](int i) {  // MFMA i: ks = i/4, db = i%4
+      const char* p = vb + vr[i & 3] + (i >> 2) * 16 * 256;
+      const s16x4 lo = tr_read(p);
+      const s16x4 hi = tr_read(p + 8 * 256);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    vf[0] = vread(0);
+    vf[1] = vread(1);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(buf + vr[db][ks]);
-        oacc[db] = mfma_bf16(va, pf[ks], oacc[db]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) vf[(i + 2) % 3] = vread(i + 2);
+      oacc[i & 3] = mfma_bf16(vf[i % 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  auto step = [&](char* cur, char* nxt, int t) {
-    if (t + 1 < ntiles) load_tile(t + 1);
-    if (!CAUSAL || t * BN <= wave_last_row) compute(cur, t);
-    if (t + 1 < ntiles) store_tile(nxt);
+  // Prologue: K(0), V(0), K(1) in LDS; scores of tile 0.
+  load_k(0, K0);
+  load_v(0, V0);
+  if (ntiles > 1) load_k(1, K1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  Scores sa, sb;
+  scores(K0, sa);
+  __syncthreads();  // K0 is refilled below
+
+  // Iteration t: LDS holds K(t+1) and V(t); it loads K(t+2) and V(t+1) into the
+  // buffers that held K(t) and V(t-1), both consumed before the last barrier.
+  // At the last tile the scores of the (absent) next tile are computed from
+  // stale LDS data and never used.
+  auto iter = [&](int t, Scores& cur, Scores& nxt, char* kcur, char* knext, char* vcur,
+                  char* vnext) {
+    if (t + 2 < ntiles) load_k(t + 2, kcur);
+    if (t + 1 < ntiles) load_v(t + 1, vnext);
+    if (active(t)) tile(t, cur, nxt, knext, vcur);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-
-  load_tile(0);
-  store_tile(smem);
-  __syncthreads();
   for (int t = 0; t < ntiles; t += 2) {
-    step(smem, smem + kStage, t);
-    if (t + 1 < ntiles) step(smem + kStage, smem, t + 1);
+    iter(t, sa, sb, K0, K1, V0, V1);
+    if (t + 1 < ntiles) iter(t + 1, sb, sa, K1, K0, V1, V0);
   }
 
   // ---- epilogue: O = acc / l (bf16), lse = m + ln l.
