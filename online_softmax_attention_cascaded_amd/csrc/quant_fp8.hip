@@ -5,8 +5,16 @@
 // between the abs-max reduction and the cast, so HBM sees it exactly once. The
 // abs-max is an integer max over the bf16 magnitude bits (for non-negative
 // values the bit pattern orders like the value). The scale is
-// fp32(absmax / 448) and every code is e4m3(fp32(x / scale)), both with
-// correctly rounded division, then round-to-nearest-even with saturation.
+// s = fp32(absmax / 448) and every code is e4m3(fp32(x / s)) with the
+// quotient correctly rounded: r = RN(1/s) once per row, then q = RN(x r),
+// e = x - s q (exact, by fma) and RN(q + e r), which is the correctly rounded
+// x / s whenever r is the correctly rounded reciprocal (Markstein's theorem for
+// division by a reciprocal with one correction step). |x / s| <= 448 (1 + 2^-23)
+// so nothing overflows; underflow can only touch quotients far below the
+// smallest e4m3 step, whose code is 0 either way. A row so small that 1/s
+// overflows takes plain division instead. The e4m3 cast is the hardware
+// round-to-nearest-even conversion (v_cvt_pk_fp8_f32); |x / s| stays below 464,
+// so no value reaches the range where saturation would matter.
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
 
@@ -40,22 +48,42 @@ __global__ __launch_bounds__(256) void absmax_quant_kernel(const uint16_t* __res
   for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, kWave));
 
   const float a = __uint_as_float(amax << 16);
-  const float s = a / 448.f;
-  if (lane == 0) scale[row] = s;
+  const float sc = a / 448.f;
+  if (lane == 0) scale[row] = sc;
+  const float rcp = (sc > 0.f) ? 1.f / sc : 0.f;
 
   u32x2* qr = reinterpret_cast<u32x2*>(q + (size_t)row * cols);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int idx = lane + 64 * c;
     if (idx >= nchunks) continue;
-    uint32_t code[8];
+    float y[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      code[2 * e] = (s > 0.f) ? e4m3_encode(bf16_lo(ch[c][e]) / s) : 0u;
-      code[2 * e + 1] = (s > 0.f) ? e4m3_encode(bf16_hi(ch[c][e]) / s) : 0u;
+      y[2 * e] = bf16_lo(ch[c][e]);
+      y[2 * e + 1] = bf16_hi(ch[c][e]);
     }
-    u32x2 w = {code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
-               code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24)};
+    if (rcp <= 3.4e38f) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float q0 = y[j] * rcp;
+        const float r = fmaf(-sc, q0, y[j]);
+        // The correction would turn -0 into +0; every other quotient already
+        // has the sign of x.
+        y[j] = __builtin_copysignf(fmaf(r, rcp, q0), y[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = y[j] / sc;
+    }
+    u32x2 w = {0u, 0u};
+    if (sc > 0.f) {
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+      w = u32x2{(uint32_t)lo, (uint32_t)hi};
+    }
     qr[idx] = w;
   }
 }

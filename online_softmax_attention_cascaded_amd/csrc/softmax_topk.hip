@@ -3,94 +3,146 @@
 // softmax", abstract: softmax and top-k fused).
 //
 // One wave per row; a 256-expert row is one 16-byte load per lane, so the row
-// never leaves registers. Each lane first reduces its own values to an
-// online-softmax state (m, l); the 64 lane states are then merged pairwise by
-// rescaling to the larger max, exactly as partial states merge across blocks
-// (cue 21). Top-k is k rounds of a wavefront argmax on (value, index) with ties
-// to the lower index; ranking by the fp32 logit equals ranking by probability
-// because softmax is strictly increasing. The top-1 logit is the row max, so
-// the selected weights are exp(x_i - max) divided either by their own sum
-// (renormalised) or by the merged denominator.
+// never leaves registers (the non-incremental form, which the transcript notes
+// is the faster one whenever the reduced axis fits on chip, cue 45). Logits are
+// mapped to order-preserving unsigned keys, so ranking, ties and the wave
+// reductions are integer operations. Top-k is k rounds of: each lane's best
+// untaken key (lowest index among equals), a wavefront max by DPP within rows
+// of 16 lanes and a scalar max across the four rows, then the lowest expert
+// index among the lanes holding that key. Ranking by the fp32 logit is the
+// same as ranking by probability because softmax is strictly increasing. The
+// top-1 logit is the row max, so the selected weights are exp(x_i - max),
+// divided by their own sum (renormalised) or by the row's denominator.
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
 
 namespace rf {
 namespace {
 
+// Order-preserving map of a finite fp32 value to uint32 (-0 is folded onto +0
+// first, so equal values have equal keys).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x + 0.f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// DPP controls (gfx9): quad permutations, half-row and row mirrors.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Max over the 64 lanes of the wave (result uniform).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp<kDppXor1>(v));
+  v = max(v, dpp<kDppXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));
+  v = max(v, dpp<kDppMirror>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp<kDppXor1>(v));
+  v = min(v, dpp<kDppXor2>(v));
+  v = min(v, dpp<kDppHalfMirror>(v));
+  v = min(v, dpp<kDppMirror>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return min(min(r0, r1), min(r2, r3));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __builtin_bit_cast(float, dpp<kDppXor1>(__builtin_bit_cast(uint32_t, v)));
+  v += __builtin_bit_cast(float, dpp<kDppXor2>(__builtin_bit_cast(uint32_t, v)));
+  v += __builtin_bit_cast(float, dpp<kDppHalfMirror>(__builtin_bit_cast(uint32_t, v)));
+  v += __builtin_bit_cast(float, dpp<kDppMirror>(__builtin_bit_cast(uint32_t, v)));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 template <int NC>  // 16-byte chunks (4 experts) per lane
 __global__ __launch_bounds__(256) void softmax_topk_kernel(const float* __restrict__ logits, int T,
                                                            int E, int k, int renorm,
                                                            float* __restrict__ weights,
                                                            int32_t* __restrict__ indices) {
+  constexpr int NV = 4 * NC;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= T) return;  // uniform per wave
   const float* x = logits + (size_t)row * E;
 
-  float val[4 * NC];
+  // Value j of this lane is expert 4 (lane + 64 (j / 4)) + j % 4; padding keys are 0.
+  uint32_t key[NV];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int chunk = lane + 64 * c;
-    f32x4 w = {kNegInf, kNegInf, kNegInf, kNegInf};
-    if (4 * chunk < E) w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x) + chunk);
+    f32x4 w = {0.f, 0.f, 0.f, 0.f};
+    const bool in = 4 * chunk < E;
+    if (in) w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x) + chunk);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) val[4 * c + e] = w[e];
-  }
-  auto expert = [&](int j) { return 4 * (lane + 64 * (j >> 2)) + (j & 3); };
-
-  // Denominator, only needed when the weights are not renormalised.
-  float m = kNegInf, l = 0.f;
-  if (!renorm) {
-#pragma unroll
-    for (int j = 0; j < 4 * NC; ++j) m = fmaxf(m, val[j]);
-#pragma unroll
-    for (int j = 0; j < 4 * NC; ++j) l += (val[j] == kNegInf) ? 0.f : fast_exp2((val[j] - m) * kLog2e);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float m2 = __shfl_xor(m, o, kWave), l2 = __shfl_xor(l, o, kWave);
-      merge_ml(m, l, m2, l2);
-    }
+    for (int e = 0; e < 4; ++e) key[4 * c + e] = in ? order_key(w[e]) : 0u;
   }
 
   uint32_t taken = 0;
-  float top = 0.f, esum = 0.f, my_e = 0.f;
-  int my_i = 0;
+  uint32_t top = 0;        // key of the row max (rank 0)
+  uint32_t my_key = 0;     // lane r keeps the key and index of rank r
+  int my_idx = 0;
   for (int r = 0; r < k; ++r) {
-    float bv = kNegInf;
-    int bi = 0x7fffffff;
+    // This lane's best untaken key; the lowest index wins among equals because
+    // values are scanned in index order and only a strictly larger key replaces.
+    uint32_t bk = 0;
+    int bj = 0;
 #pragma unroll
-    for (int j = 0; j < 4 * NC; ++j) {
-      const int id = expert(j);
-      const bool better = val[j] > bv || (val[j] == bv && id < bi);
-      if (!((taken >> j) & 1u) && id < E && better) {
-        bv = val[j];
-        bi = id;
+    for (int j = 0; j < NV; ++j) {
+      const uint32_t kj = ((taken >> j) & 1u) ? 0u : key[j];
+      if (kj > bk) {
+        bk = kj;
+        bj = j;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+    const uint32_t wk = wave_max_u32(bk);
+    const uint64_t holders = __ballot(bk == wk);
+    int widx;
+    if (__popcll(holders) == 1) {
+      const int wl = __ffsll((long long)holders) - 1;
+      widx = __builtin_amdgcn_readlane(4 * (lane + 64 * (bj >> 2)) + (bj & 3), wl);
+    } else {
+      const uint32_t cand = (bk == wk) ? (uint32_t)(4 * (lane + 64 * (bj >> 2)) + (bj & 3)) : 0xffffffffu;
+      widx = (int)wave_min_u32(cand);
     }
-    // (bv, bi) is now the same in every lane; its owner marks it taken.
-    const int chunk = bi >> 2;
-    if ((chunk & 63) == lane) taken |= 1u << (4 * (chunk >> 6) + (bi & 3));
-    if (r == 0) top = bv;
-    const float e = expf(bv - top);
-    esum += e;
+    // The owner of expert widx marks it taken.
+    const int wchunk = widx >> 2;
+    if ((wchunk & 63) == lane) taken |= 1u << (4 * (wchunk >> 6) + (widx & 3));
+    if (r == 0) top = wk;
     if (lane == r) {
-      my_e = e;
-      my_i = bi;
+      my_key = wk;
+      my_idx = widx;
     }
   }
+
+  const float m = key_value(top);
+  const float e = (lane < k) ? expf(key_value(my_key) - m) : 0.f;
+  float denom;
+  if (renorm) {
+    denom = wave_sum_f32(e);
+  } else {
+    float l = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (key[j] != 0u) l += fast_exp2((key_value(key[j]) - m) * kLog2e);
+    denom = wave_sum_f32(l);
+  }
   if (lane < k) {
-    const float w = renorm ? my_e / esum : my_e / l;
-    weights[(size_t)row * k + lane] = w;
-    indices[(size_t)row * k + lane] = my_i;
+    weights[(size_t)row * k + lane] = e / denom;
+    indices[(size_t)row * k + lane] = my_idx;
   }
 }
 

@@ -44,6 +44,39 @@ def test_quantiser_rounding_edges():
     assert np.array_equal(q.cpu().numpy(), q_ref)
 
 
+def _all_bf16_rows(amax_values, seed):
+    """Rows holding every positive bf16 pattern up to each abs-max value A (random
+    signs), A itself first in every row, zero-padded to 8192 columns."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for a in amax_values:
+        abits = int(torch.tensor([a], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).item()) & 0xFFFF
+        pats = np.arange(1, abits, dtype=np.uint32)
+        vals = (pats << 16).view(np.float32) * rng.choice([-1.0, 1.0], size=len(pats)).astype(np.float32)
+        top = np.float32((np.uint32(abits) << 16).view(np.float32))
+        for i in range(0, len(vals), 8191):
+            row = np.zeros(8192, np.float32)
+            row[0] = top
+            part = vals[i:i + 8191]
+            row[1:1 + len(part)] = part
+            rows.append(row)
+    return torch.from_numpy(np.stack(rows)).to(torch.bfloat16)
+
+
+def test_quantiser_every_bf16_pattern():
+    """The division x / s and the e4m3 rounding on every input bit pattern a row can
+    hold, for 12 row maxima (one so small that 1/s overflows fp32)."""
+    x = _all_bf16_rows([448.0, 1.0, 3.5, 0.0078125, 1e-3, 17.25, 6.0e4, 2.0 ** -100, 123.456, 0.3,
+                        1e30, 5e-38], seed=13)
+    print_case(test="quant_all_bf16", rows=x.shape[0])
+    q, s = rf.absmax_quant_fp8(x.to(DEV))
+    q_ref, s_ref = oracle.absmax_quant(x.float().numpy())
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    got = q.cpu().numpy()
+    bad = np.argwhere(got != q_ref)
+    assert len(bad) == 0, f"{len(bad)} codes differ, first {bad[:3].tolist()}"
+
+
 @pytest.mark.parametrize("M,N,K", [(64, 64, 256), (300, 200, 512), (256, 512, 1024), (1, 3, 128)])
 def test_gemm_small(M, N, K):
     print_case(test="gemm_small", M=M, N=N, K=K)

@@ -42,6 +42,17 @@ def test_routing_ties(seed):
     _check(inputs.tie_heavy_logits(seed, 300, 64), 8, False)
 
 
+def test_routing_signed_zero_ties():
+    """-0.0 and +0.0 are equal logits: the lower index goes first."""
+    import torch
+
+    x = torch.zeros((8, 64))
+    x[:, ::2] = -0.0
+    x[:, 5] = 1.0
+    _check(x, 8, True)
+    _check(x, 8, False)
+
+
 def test_routing_empty():
     import torch
 
