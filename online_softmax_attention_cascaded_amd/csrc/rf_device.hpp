@@ -31,6 +31,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
+// Workgroup barrier for handing LDS contents between waves. It waits for this
+// wave's own LDS operations and then meets the other waves; unlike
+// __syncthreads(), whose fence also drains every outstanding global and buffer
+// load, loads issued for later pipeline stages stay in flight. Loads that write
+// LDS directly are counted by vmcnt: wait for them explicitly before calling.
+// The memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // bf16 <-> fp32. A bf16 value is the upper half of an fp32 bit pattern, so the
 // widening is exact; the narrowing uses the hardware round-to-nearest-even
 // convert (v_cvt_pk_bf16_f32 on gfx950).
