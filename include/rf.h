@@ -58,7 +58,9 @@ typedef enum { RF_F32 = 0, RF_BF16 = 1 } rf_dtype;
  * K/V tiles with running (m, l, acc) per query row (transcript cues 15-19).
  *
  *   dt     RF_BF16: q, k, v, o are bf16, math in fp32 (MFMA for both
- *          contractions); RF_F32: all fp32 (FMA). Head size d in {64, 128}.
+ *          contractions), d == 128 and one head's K (or V) under 2 GiB
+ *          (Lk * d * 2 < 2^31, else RF_ERR_UNSUPPORTED); RF_F32: all fp32
+ *          (FMA), d in {64, 128}.
  *   q      [B, Hq, Lq, d]      k, v  [B, Hkv, Lk, d]     o  [B, Hq, Lq, d] (dt)
  *   lse    [B, Hq, Lq] fp32 or NULL: m + ln(l) of the scaled scores.
  *   Hq % Hkv == 0; query head h reads key/value head h / (Hq / Hkv).
@@ -80,7 +82,8 @@ rf_status rf_attn_fwd(rf_dtype dt, const void* q, const void* k, const void* v, 
  * all fp32 (transcript cue 39: Multi-Segment; cue 21: the states merge).
  *
  *   dt must be RF_BF16: q [B, Hq, d], k, v [B, Hkv, Lk, d] bf16; d == 128;
- *   Hq % Hkv == 0 and Hq / Hkv <= 16; S >= 1; Lk >= 1.
+ *   Hq % Hkv == 0 and Hq / Hkv <= 16; S >= 1; Lk >= 1; one head's K (or V)
+ *   under 2 GiB (Lk * d * 2 < 2^31, else RF_ERR_UNSUPPORTED).
  */
 rf_status rf_attn_decode_split(rf_dtype dt, const void* q, const void* k, const void* v,
                                float* part_m, float* part_l, float* part_acc, int B, int Hq,

@@ -14,50 +14,75 @@
 // "Merging partial states across blocks (FlashDecoding-style)").
 //
 // Decode is bound by HBM bandwidth: every K/V byte is read exactly once per
-// GQA group. Both contractions use v_mfma_f32_16x16x32_bf16 with the group's
-// query heads in the N (or M) dimension, so bf16 K/V never need a VALU widening.
-// K rows go straight from global memory into the A operand (16-byte loads);
-// V rows are transposed through a per-wave LDS buffer so the B operand of
-// O = P V gets its 8 keys with one 16-byte read.
+// GQA group, and throughput is set by how many bytes each CU keeps in flight.
+// Both contractions use v_mfma_f32_16x16x32_bf16 with the group's query heads
+// in the N (or M) dimension, so bf16 K/V never need a VALU widening.
+//  - K rows go straight from global memory into the A operand of S^T = K Q^T
+//    (16-byte loads), two steps ahead of their use, in three register sets
+//    whose roles rotate with a 3-way unrolled loop (no register copies, so no
+//    wait on the newest loads).
+//  - V rows are loaded one step ahead straight into a two-slot LDS ring per
+//    wave (buffer loads to LDS, no registers), in their natural row-major
+//    layout; the B operand of O = P V is read back transposed with
+//    ds_read_b64_tr_b16, four keys of one column per lane per read.
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
+
+#include <type_traits>
 
 namespace rf {
 namespace {
 
 constexpr int D = 128;
-constexpr int STEP = 32;  // keys per wave step
-constexpr int NW = 4;     // waves per workgroup
-constexpr int kVtBytes = D * STEP * 2;  // one transposed V step, 8 KB
+constexpr int STEP = 32;                  // keys per wave step
+constexpr int NW = 4;                     // waves per workgroup
+constexpr int kVSlot = STEP * D * 2;      // one step of V rows, 8 KB
+constexpr int kSmem = NW * 2 * kVSlot;    // two slots per wave, 64 KB
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// ds_read_b64_tr_b16 through inline asm. The compiler cannot tell whether a
+// read from LDS overlaps a pending buffer-to-LDS load, so for the builtin it
+// drains every outstanding load first (including the prefetches of later
+// steps). The asm form is invisible to that analysis; its results become
+// usable only through tr_wait(), which waits for the LDS reads explicitly.
+__device__ __forceinline__ u32x2 tr_read(uint32_t lds_addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr));
+  return r;
+}
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Transposed V step: row d holds the step's 32 keys (64 bytes, four 16-byte
-// chunks, XOR-swizzled by d so 16 consecutive d rows hit distinct banks).
-__device__ __forceinline__ int vt_off(int d, int key4) {
-  return d * 64 + (((key4 >> 3) ^ ((d >> 1) & 3)) << 4) + ((key4 >> 2) & 1) * 8;
-}
+// V slot layout: row r (a key) holds 256 bytes = 16 chunks of 16 bytes; logical
+// chunk c sits at physical chunk c ^ vswz(r). vswz is even, so the chunk pairs
+// {2n, 2n + 1} (one 16-column block) stay together, and the transposed reads of
+// 32 consecutive lanes (rows 8g + 0..3 and 8g + 8 + 0..3 of a slot, one 32-byte
+// pair each) land on distinct banks.
+__device__ __forceinline__ int vswz(int row) { return 2 * (row & 3) + 8 * ((row >> 3) & 1); }
+
+template <int V>
+using ic = std::integral_constant<int, V>;
 
 struct KRegs {
   u32x4 k[2][4];  // A operand of S^T = K Q^T: [key block][d step]
-};
-struct VRegs {
-  u32x4 v[2][4];  // V rows: [key group half][key within group of 4]
 };
 
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ part_m, float* __restrict__ part_l,
     float* __restrict__ part_acc, int Hq, int Hkv, int Lk, int S, int seg_len, float scale) {
-  __shared__ __attribute__((aligned(16))) char smem[NW * kVtBytes + 512];
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
 
   const int s = blockIdx.x % S;
   const int bhk = blockIdx.x / S;  // b * Hkv + hk
   const int b = bhk / Hkv, hk = bhk - b * Hkv;
   const int G = Hq / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to M0
   const int g = lane >> 4, lq = lane & 15;
 
   const int t0 = min(s * seg_len, Lk), t1 = min(t0 + seg_len, Lk);
@@ -78,72 +103,86 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     }
   }
 
+  // Every load below is issued unconditionally; a step past the segment gets
+  // the scalar offset kv_end, the byte size of one head's K (or V), so its
+  // loads read zeros without touching memory. That keeps the number of loads
+  // in flight, and so every wait count, fixed.
+  const int kv_end = Lk * D * 2;
+  auto soff_of = [&](int step) {
+    return __builtin_amdgcn_readfirstlane(step < nsteps ? (t0 + step * STEP) * 256 : kv_end);
+  };
+
   // K row loaded by this lane for key block kb: row i = lq of the block holds key
   // 8*(lq/4) + 4*kb + lq%4, so lane group g ends up with keys 8g..8g+7 of the step.
-  const int krow0 = 8 * (lq >> 2) + (lq & 3);
-  auto load_k = [&](int step, KRegs& r) {
-    const int kbase = t0 + step * STEP;
+  // Buffer loads: 32-bit offsets, and rows past Lk read as zero (masked below).
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)kv_end);
+  int kvo[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = min(kbase + krow0 + 4 * kb, Lk - 1);
+  for (int kb = 0; kb < 2; ++kb) kvo[kb] = (8 * (lq >> 2) + (lq & 3) + 4 * kb) * 256 + 16 * g;
+  auto load_k = [&](int step, KRegs& r) {
+    const int soff = soff_of(step);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds)
-        r.k[kb][ds] = *reinterpret_cast<const u32x4*>(kp + (size_t)key * D + 32 * ds + 8 * g);
-    }
+        r.k[kb][ds] = buf_load16(krs, kvo[kb] + 64 * ds, soff);
   };
-  auto load_v = [&](int step, VRegs& r) {
-    const int kbase = t0 + step * STEP;
+
+  // V step -> LDS slot: eight 1 KB loads, load i covers rows 4i..4i+3 of the
+  // step; lane l writes physical chunk l % 16 of row 4i + l / 16, so it fetches
+  // the logical chunk (l % 16) ^ vswz(row). Rows past Lk read as zero (their
+  // scores are masked anyway); rows past the segment are real keys whose
+  // weights are 0.
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)kv_end);
+  int vvo[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int kg = g + 4 * i;
+  for (int i = 0; i < 8; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    vvo[i] = row * 256 + (((lane & 15) ^ vswz(row)) << 4);
+  }
+  char* vslots = smem + wave * 2 * kVSlot;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)vslots;  // LDS byte address
+  auto issue_v = [&](int step, int slot) {
+    char* dst = vslots + __builtin_amdgcn_readfirstlane(slot * kVSlot);
+    const int soff = soff_of(step);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = min(kbase + 4 * kg + j, Lk - 1);
-        r.v[i][j] = *reinterpret_cast<const u32x4*>(vp + (size_t)key * D + 8 * lq);
-      }
-    }
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + i * 1024), 16, vvo[i], soff, 0, 0);
   };
+  // Transposed read of d block nb: lane (g, lq) points at row 8g + lq/4 (+4 for
+  // the second read), columns 16 nb + 4 (lq % 4) .. + 3; the LDS returns to lane
+  // lq the four keys of column 16 nb + lq.
+  int vto[8];
+  {
+    const int row = 8 * g + (lq >> 2);
+    const int sw = vswz(row) >> 1;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) vto[nb] = row * 256 + ((nb ^ sw) << 5) + 8 * (lq & 3);
+  }
 
   float m_run = kNegInf, l_run = 0.f;  // statistics of query head lq
   f32x4 oacc[8];                       // O[q = 4g + r][d = 16*nb + lq]
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) oacc[nb] = f32x4{};
 
-  // K rows are loaded two steps ahead of their use and V rows one step ahead
-  // (three K register sets and two V sets in rotation).
-  KRegs kcur, knxt, knxt2;
-  VRegs vcur, vnxt;
-  // Each wave owns an 8 KB slice of LDS for its transposed V step and touches
-  // no other wave's slice, so the loop needs no workgroup barrier: LDS
-  // operations of one wave execute in issue order, and the fences below only
-  // stop the compiler from moving the reads above the writes (or the next
-  // step's writes above this step's reads).
-  char* vt = smem + wave * kVtBytes;
-  if (wave < nsteps) {
-    load_k(wave, kcur);
-    load_v(wave, vcur);
-  }
-  if (wave + NW < nsteps) load_k(wave + NW, knxt);
-  for (int step = wave; step < nsteps; step += NW) {
-    if (step + NW < nsteps) load_v(step + NW, vnxt);
-    if (step + 2 * NW < nsteps) load_k(step + 2 * NW, knxt2);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int kg = g + 4 * i;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t a0 = vcur.v[i][0][e], a1 = vcur.v[i][1][e];
-        const uint32_t a2 = vcur.v[i][2][e], a3 = vcur.v[i][3][e];
-        const int d = 8 * lq + 2 * e;
-        u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        *reinterpret_cast<u32x2*>(vt + vt_off(d, 4 * kg)) = lo;
-        *reinterpret_cast<u32x2*>(vt + vt_off(d + 1, 4 * kg)) = hi;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  KRegs ks[3];
+  // Prologue, in the order the waits below assume: K(0), V(0), K(1).
+  load_k(wave, ks[0]);
+  issue_v(wave, 0);
+  load_k(wave + NW, ks[1]);
+
+  // Iteration j handles step wave + NW j with K set j % 3 and V slot j % 2. It
+  // first issues V(j + 1) and K(j + 2), so inside the unrolled loop exactly 24
+  // loads are issued after V(j): K(j + 1), V(j + 1), K(j + 2), eight each. In
+  // the tail iterations after the loop some of those K loads feed nothing and
+  // the compiler drops them, so the tail waits for all loads instead.
+  auto body = [&](auto cset, auto tail_c, int j) {
+    constexpr int C = decltype(cset)::value;
+    constexpr bool TAIL = decltype(tail_c)::value != 0;
+    const int step = wave + NW * j;
+    issue_v(step + NW, (j + 1) & 1);
+    load_k(step + 2 * NW, ks[(C + 2) % 3]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetches ahead of the math
     const int kbase = t0 + step * STEP;
     // ---- S^T = K Q^T: sacc[kb][r] is the score of key kbase + 8g + 4kb + r, head lq.
     f32x4 sacc[2];
@@ -151,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     for (int kb = 0; kb < 2; ++kb) {
       f32x4 a = f32x4{};
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) a = mfma16(__builtin_bit_cast(bf16x8, kcur.k[kb][ds]), qf[ds], a);
+      for (int ds = 0; ds < 4; ++ds) a = mfma16(__builtin_bit_cast(bf16x8, ks[C].k[kb][ds]), qf[ds], a);
       sacc[kb] = a;
     }
     float mx = kNegInf;
@@ -188,28 +227,56 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     rs += __shfl_xor(rs, 32, kWave);
     l_run = alpha * l_run + rs;
     m_run = m_new;
-    // ---- rescale O rows 4g + r by their head's alpha, then O += P V.
     float ar[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r, kWave);
+    // ---- wait for V(j) to land in its slot (tied to l_run so that the wait
+    // stays behind the softmax instead of being hoisted into the products).
+    if constexpr (TAIL)
+      asm volatile("s_waitcnt vmcnt(0)" : "+v"(l_run) : : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(24)" : "+v"(l_run) : : "memory");
+    // ---- O += P V: B operands of the eight d blocks (keys 8g..8g+3, then
+    // 8g+4..8g+7, of column 16 nb + lq), read transposed from the slot.
+    const uint32_t vs = lds_base + (uint32_t)((j & 1) * kVSlot);
+    u32x2 vt[8][2];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
+      vt[nb][0] = tr_read(vs + vto[nb]);
+      vt[nb][1] = tr_read(vs + vto[nb] + 1024);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vt[0][0]), "+v"(vt[0][1]), "+v"(vt[1][0]), "+v"(vt[1][1]),
+                   "+v"(vt[2][0]), "+v"(vt[2][1]), "+v"(vt[3][0]), "+v"(vt[3][1]),
+                   "+v"(vt[4][0]), "+v"(vt[4][1]), "+v"(vt[5][0]), "+v"(vt[5][1]),
+                   "+v"(vt[6][0]), "+v"(vt[6][1]), "+v"(vt[7][0]), "+v"(vt[7][1]));
+    // rescale O rows 4g + r by their head's alpha, then accumulate.
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const bf16x8 vb = __builtin_bit_cast(
+          bf16x8, u32x4{vt[nb][0][0], vt[nb][0][1], vt[nb][1][0], vt[nb][1][1]});
 #pragma unroll
       for (int r = 0; r < 4; ++r) oacc[nb][r] *= ar[r];
-      const int d = 16 * nb + lq;
-      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vt + vt_off(d, 8 * g));
       oacc[nb] = mfma16(pa, vb, oacc[nb]);
       oacc[nb] = mfma16(pa_lo, vb, oacc[nb]);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    kcur = knxt;
-    knxt = knxt2;
-    vcur = vnxt;
+  };
+
+  // This wave's steps: wave, wave + NW, ... below nsteps.
+  const int niter = (nsteps - wave + NW - 1) / NW;
+  int j = 0;
+  for (; j + 3 <= niter; j += 3) {
+    body(ic<0>{}, ic<0>{}, j);
+    body(ic<1>{}, ic<0>{}, j + 1);
+    body(ic<2>{}, ic<0>{}, j + 2);
   }
+  if (j < niter) body(ic<0>{}, ic<1>{}, j);
+  if (j + 1 < niter) body(ic<1>{}, ic<1>{}, j + 1);
 
   // ---- merge the four waves' states (same rule as the merge across segments).
+  // The loads issued past the end still write their (zero) rows into the V
+  // slots: drain them before the slots are reused.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   float* sm_m = reinterpret_cast<float*>(smem);      // [NW][16]
   float* sm_l = sm_m + NW * 16;                       // [NW][16]

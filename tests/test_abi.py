@@ -82,6 +82,7 @@ def attn(lib, dt=BF16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=
         (dict(d=96), UNSUPPORTED),
         (dict(dt=F32, d=96), UNSUPPORTED),
         (dict(d=64), UNSUPPORTED),
+        (dict(Lk=1 << 23), UNSUPPORTED),     # one head's K/V reaches 2 GiB
     ],
 )
 def test_attn_validation(lib, kw, expect):
@@ -111,6 +112,7 @@ def decode(lib, dt=BF16, q=FAKE, k=FAKE, v=FAKE, m=FAKE, l=FAKE, acc=FAKE, B=1, 
         (dict(dt=F32), UNSUPPORTED),
         (dict(d=64), UNSUPPORTED),
         (dict(Hq=34, Hkv=2), UNSUPPORTED),
+        (dict(Lk=1 << 23), UNSUPPORTED),     # one head's K/V reaches 2 GiB
     ],
 )
 def test_decode_validation(lib, kw, expect):
