@@ -319,72 +319,74 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   }
 }
 
-// One workgroup per row. Thread (slice, c) folds the states s = slice,
-// slice + nslices, ... of its row into a running (m, l, acc[4 columns]) with the
-// same rescale-and-add rule (cue 21), then slice 0 merges the slices' states
-// from LDS and writes the row.
-__global__ __launch_bounds__(256) void merge_states_kernel(const float* __restrict__ part_m,
-                                                           const float* __restrict__ part_l,
-                                                           const float* __restrict__ part_acc,
-                                                           int rows, int S, int d, int out_bf16,
-                                                           void* __restrict__ o,
-                                                           float* __restrict__ lse) {
-  __shared__ float sm_m[256], sm_l[256];
-  __shared__ f32x4 sm_acc[256];
-  const int row = blockIdx.x;
-  const int nd4 = d >> 2;
-  const int nslices = 256 / nd4;
-  const int tid = threadIdx.x;
-  const int slice = tid / nd4, c = tid - slice * nd4;
-  const bool worker = slice < nslices;
-  const float* mrow = part_m + (size_t)row * S;
-  const float* lrow = part_l + (size_t)row * S;
-  const float* arow = part_acc + (size_t)row * S * d + 4 * c;
-  float m = kNegInf, l = 0.f;
-  f32x4 acc = f32x4{};
-  if (worker) {
-    for (int s = slice; s < S; s += nslices) {
-      const float ms = mrow[s];
-      if (ms == kNegInf) continue;  // empty segment: the identity
-      const float ls = lrow[s];
-      const f32x4 as = *reinterpret_cast<const f32x4*>(arow + (size_t)s * d);
-      const float mn = fmaxf(m, ms);
-      const float a = (m == kNegInf) ? 0.f : fast_exp2((m - mn) * kLog2e);
-      const float b = fast_exp2((ms - mn) * kLog2e);
-      l = l * a + ls * b;
-      acc = acc * a + as * b;
-      m = mn;
+// Fold one partial state (ms, ls, as) into a running (m, l, acc): both sides
+// are rescaled to the larger max; a side with max -inf is empty and has weight 0.
+__device__ __forceinline__ void fold_state(float& m, float& l, f32x4& acc, float ms, float ls,
+                                           const f32x4& as) {
+  const float mn = fmaxf(m, ms);
+  const float a = (m == kNegInf) ? 0.f : fast_exp2((m - mn) * kLog2e);
+  const float b = (ms == kNegInf) ? 0.f : fast_exp2((ms - mn) * kLog2e);
+  l = l * a + ls * b;
+  acc = acc * a + as * b;
+  m = mn;
+}
+
+// One wave per row, no LDS. Lane (h, c) covers columns 4c..4c+3 of a
+// 128-column block and folds the states s = h, h + 2, ... with the rescale-
+// and-add rule (cue 21), loading kChunk states at a time so their loads are
+// in flight together; the two half-waves then merge their states and lanes of
+// the first half write the row. Blocks of 128 columns repeat for d > 128.
+constexpr int kChunk = 8;
+
+__global__ __launch_bounds__(64) void merge_states_kernel(const float* __restrict__ part_m,
+                                                          const float* __restrict__ part_l,
+                                                          const float* __restrict__ part_acc,
+                                                          int S, int d, int out_bf16,
+                                                          void* __restrict__ o,
+                                                          float* __restrict__ lse) {
+  const size_t row = blockIdx.x;
+  const int lane = threadIdx.x, h = lane >> 5, c = lane & 31;
+  const float* mrow = part_m + row * S;
+  const float* lrow = part_l + row * S;
+  const float* arow = part_acc + row * S * d;
+  for (int c0 = 0; c0 < d; c0 += 128) {
+    const int col = c0 + 4 * c;
+    const bool act = col < d;
+    float m = kNegInf, l = 0.f;
+    f32x4 acc = f32x4{};
+    for (int s0 = 0; s0 < S; s0 += 2 * kChunk) {
+      float ms[kChunk], ls[kChunk];
+      f32x4 as[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        const int s = s0 + h + 2 * i;
+        const int sc = min(s, S - 1);  // loads stay unconditional; out-of-range states are empty
+        ms[i] = mrow[sc];
+        ls[i] = lrow[sc];
+        as[i] = act ? *reinterpret_cast<const f32x4*>(arow + (size_t)sc * d + col) : f32x4{};
+        if (s >= S) ms[i] = kNegInf;
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) fold_state(m, l, acc, ms[i], ls[i], as[i]);
     }
-    sm_acc[tid] = acc;
-    if (c == 0) {
-      sm_m[slice] = m;
-      sm_l[slice] = l;
+    // Merge the other half-wave's state (lane c + 32 holds the same columns).
+    const float m2 = __shfl_xor(m, 32, kWave), l2 = __shfl_xor(l, 32, kWave);
+    f32x4 a2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a2[e] = __shfl_xor(acc[e], 32, kWave);
+    fold_state(m, l, acc, m2, l2, a2);
+    if (h == 0 && act) {
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+      acc *= inv;
+      if (out_bf16) {
+        const u32x2 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + row * d + col) = w;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(o) + row * d + col) = acc;
+      }
     }
+    if (lse && lane == 0 && c0 == 0) lse[row] = (m == kNegInf) ? kNegInf : m + logf(l);
   }
-  __syncthreads();
-  if (slice != 0) return;
-  float ms = kNegInf;
-  for (int j = 0; j < nslices; ++j) ms = fmaxf(ms, sm_m[j]);
-  float lt = 0.f;
-  f32x4 at = f32x4{};
-  if (ms != kNegInf) {
-    for (int j = 0; j < nslices; ++j) {
-      const float mj = sm_m[j];
-      if (mj == kNegInf) continue;
-      const float w = fast_exp2((mj - ms) * kLog2e);
-      lt += w * sm_l[j];
-      at += w * sm_acc[j * nd4 + c];
-    }
-  }
-  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-  at *= inv;
-  if (out_bf16) {
-    u32x2 w = {pack_bf16x2(at[0], at[1]), pack_bf16x2(at[2], at[3])};
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + (size_t)row * d + 4 * c) = w;
-  } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(o) + (size_t)row * d + 4 * c) = at;
-  }
-  if (lse && c == 0) lse[row] = (ms == kNegInf) ? kNegInf : ms + logf(lt);
 }
 
 }  // namespace
@@ -405,8 +407,8 @@ hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
 hipError_t launch_merge_states(const float* part_m, const float* part_l, const float* part_acc,
                                int rows, int S, int d, int out_bf16, void* o, float* lse,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(merge_states_kernel, dim3(rows), dim3(256), 0, stream, part_m, part_l,
-                     part_acc, rows, S, d, out_bf16, o, lse);
+  hipLaunchKernelGGL(merge_states_kernel, dim3(rows), dim3(64), 0, stream, part_m, part_l,
+                     part_acc, S, d, out_bf16, o, lse);
   return hipGetLastError();
 }
 
