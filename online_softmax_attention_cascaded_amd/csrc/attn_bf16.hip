@@ -37,10 +37,10 @@ constexpr int BM = 128;                 // query rows per workgroup, 32 per wave
 constexpr int BN = 64;                  // keys per tile
 constexpr int kTileBytes = BN * D * 2;  // 16 KB per operand tile
 constexpr float kTau = 8.f;             // lazy-rescale threshold, exp2 units
+constexpr int KA = 3;                   // K fragment reads run this many MFMAs ahead
+constexpr int VA = 4;                   // V^T fragment reads run this many MFMAs ahead
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct Scores {
   f32x16 s0, s1;  // keys 0..31 and 32..63 of the tile (accumulator layout)
@@ -52,12 +52,6 @@ __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, co
 
 __device__ __forceinline__ float max3(float a, float b, float c) {
   return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
-}
-
-// Four keys (rows) of one head-size column per lane, transposed from the
-// row-major tile by the LDS (see the read-address comment in the kernel).
-__device__ __forceinline__ s16x4 tr_read(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
 template <bool CAUSAL>
@@ -192,10 +186,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
         if (key1 >= Lk || (CAUSAL && key1 > qrow)) cur.s1[r] = kNegInf;
       }
     }
-    float mx = __builtin_fmaxf(cur.s0[0], cur.s1[0]);
+    // Row max: four independent max3 chains, then the two halves of the wave.
+    float m4[4];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = max3(mx, cur.s0[r], cur.s1[r]);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    for (int j = 0; j < 4; ++j) m4[j] = __builtin_fmaxf(cur.s0[j], cur.s1[j]);
+#pragma unroll
+    for (int r = 4; r < 16; ++r) m4[r & 3] = max3(m4[r & 3], cur.s0[r], cur.s1[r]);
+    const float mx = half_swap_max(__builtin_fmaxf(__builtin_fmaxf(m4[0], m4[1]), __builtin_fmaxf(m4[2], m4[3])));
     const float mxc = mx * c;
     if (t == 0) {
       m_c = mxc;  // every row sees key 0, so this is finite
@@ -209,29 +206,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
     }
-    // ---- from here on one basic block, in a fixed issue order: MFMA i of the
-    // scores of tile t+1 (K fragment read three steps ahead), then the VALU work
-    // for probabilities 2i, 2i+1 of tile t (2 fma, 2 exp2, 1 bf16 pack, 2 adds);
-    // sched_barrier fences keep the compiler from regrouping them. Then the 16
-    // P V MFMAs, each with its two transposing V reads issued two MFMAs ahead.
+    // ---- one basic block: the 16 score MFMAs of tile t+1, each K fragment read
+    // KA MFMAs ahead (the fences keep every read next to its MFMA), and the
+    // probabilities of tile t (2 fma, 2 exp2, 1 bf16 pack, 2 adds per pair). The
+    // compiler issues the exponentials after the score MFMAs; they overlap with
+    // the other wave on the SIMD (steering them between the MFMAs measured no
+    // faster). Then the 16 P V MFMAs, each with its two transposing V reads
+    // issued VA MFMAs ahead.
     nxt.s0 = f32x16{};
     nxt.s1 = f32x16{};
-    bf16x8 kf[4];
+    bf16x8 kf[KA + 1];
     auto kread = [&](int i) {
       return *reinterpret_cast<const bf16x8*>(knext + kr[i >> 1] + (i & 1) * 32 * 256);
     };
-    kf[0] = kread(0);
-    kf[1] = kread(1);
-    kf[2] = kread(2);
+#pragma unroll
+    for (int i = 0; i < KA; ++i) kf[i] = kread(i);
     u32x4 pw[4];
     float rs = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i + 3 < 16) kf[(i + 3) & 3] = kread(i + 3);
+      if (i + KA < 16) kf[(i + KA) % (KA + 1)] = kread(i + KA);
       if (i & 1)
-        nxt.s1 = mfma_bf16(kf[i & 3], qf[i >> 1], nxt.s1);
+        nxt.s1 = mfma_bf16(kf[i % (KA + 1)], qf[i >> 1], nxt.s1);
       else
-        nxt.s0 = mfma_bf16(kf[i & 3], qf[i >> 1], nxt.s0);
+        nxt.s0 = mfma_bf16(kf[i % (KA + 1)], qf[i >> 1], nxt.s0);
       // probabilities 2i, 2i+1: k-step ks = i/4, pair jj = i%4 of P^T's B operand
       const int ks = i >> 2, jj = i & 3;
       const f32x16& src = (ks < 2) ? cur.s0 : cur.s1;
@@ -242,24 +240,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       pw[ks][jj] = pack_bf16x2(p0, p1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    rs += __shfl_xor(rs, 32, kWave);
-    l_run += rs;
-    // O^T += V^T P^T; consecutive MFMAs update different accumulators.
-    bf16x8 vf[3];
-    auto vread = [&](int i) {  // MFMA i: ks = i/4, db = i%4
-      const char* p = vb + vr[i & 3] + (i >> 2) * 16 * 256;
-      const s16x4 lo = tr_read(p);
-      const s16x4 hi = tr_read(p + 8 * 256);
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    l_run += half_swap_sum(rs);
+    // O^T += V^T P^T; consecutive MFMAs update different accumulators. MFMA i
+    // (k-step i/4, d block i%4) takes its V^T operand from two transposing
+    // reads issued VA MFMAs ahead; each MFMA waits for exactly its own reads.
+    const uint32_t va = lds_addr(vb);
+    u32x4 vf[VA + 1];
+    auto vread = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const uint32_t a = va + vr[i & 3];
+      const u32x2 lo = lds_read_tr16<(i >> 2) * 16 * 256>(a);
+      const u32x2 hi = lds_read_tr16<(i >> 2) * 16 * 256 + 8 * 256>(a);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
-    vf[0] = vread(0);
-    vf[1] = vread(1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + 2 < 16) vf[(i + 2) % 3] = vread(i + 2);
-      oacc[i & 3] = mfma_bf16(vf[i % 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
+    static_for<VA>([&](auto ic) { vf[decltype(ic)::value] = vread(ic); });
+    static_for<16>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + VA < 16) vf[(i + VA) % (VA + 1)] = vread(std::integral_constant<int, i + VA>{});
+      // reads issued after MFMA i's own: two per later MFMA already in flight
+      lds_wait_for<2 * ((15 - i) < VA ? (15 - i) : VA)>(vf[i % (VA + 1)]);
+      oacc[i & 3] = mfma_bf16(__builtin_bit_cast(bf16x8, vf[i % (VA + 1)]),
+                              __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
 
   // Prologue: K(0), V(0), K(1) in LDS; scores of tile 0.
@@ -267,10 +270,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   load_v(0, V0);
   if (ntiles > 1) load_k(1, K1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  lds_barrier();
   Scores sa, sb;
   scores(K0, sa);
-  __syncthreads();  // K0 is refilled below
+  lds_barrier();  // K0 is refilled below
 
   // Iteration t: LDS holds K(t+1) and V(t); it loads K(t+2) and V(t+1) into the
   // buffers that held K(t) and V(t-1), both consumed before the last barrier.
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     if (t + 1 < ntiles) load_v(t + 1, vnext);
     if (active(t)) tile(t, cur, nxt, knext, vcur);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    lds_barrier();
   };
   for (int t = 0; t < ntiles; t += 2) {
     iter(t, sa, sb, K0, K1, V0, V1);

@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace rf {
 
 constexpr int kWave = 64;
@@ -41,6 +44,47 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so
+// the body can use I in constant expressions (immediate offsets, register
+// indices).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// ds_read_b64_tr_b16 (gfx950 transposing LDS read) through inline asm, at LDS
+// byte address addr + OFF. Within each group of 16 lanes, lane j supplies the
+// address of four consecutive bf16 values (8 bytes); lane i receives element
+// 16 s + i (s = 0..3) of the group's 64 values taken in lane order, i.e. when
+// lane j points at row r0 + j / 4, columns c0 + 4 (j % 4) .. +3 of a row-major
+// tile, lane i receives rows r0 .. r0 + 3 of column c0 + i.
+// The builtin form makes the compiler wait for every outstanding buffer-to-LDS
+// load before the read (it cannot prove the two disjoint), which drains the
+// prefetches of later tiles. The asm form is invisible to that analysis, and
+// to the compiler's own LDS wait counting: the result may be used only after
+// lds_wait_for() has covered it.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// Wait until at most N LDS operations are outstanding (they complete in issue
+// order), and make x depend on the wait so its uses stay behind it.
+template <int N, class T>
+__device__ __forceinline__ void lds_wait_for(T& x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+
 // bf16 <-> fp32. A bf16 value is the upper half of an fp32 bit pattern, so the
 // widening is exact; the narrowing uses the hardware round-to-nearest-even
 // convert (v_cvt_pk_bf16_f32 on gfx950).
@@ -70,6 +114,18 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
+}
+
+// Sum and max over lanes l and l ^ 32 without LDS: v_permlane32_swap (gfx950)
+// applied to (x, x) returns x[l % 32] and x[32 + l % 32] in every lane l, so
+// both lanes of a pair combine the same two values in the same order.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Merge of two online-softmax statistics (m, l): both rescaled to the larger max.
