@@ -146,10 +146,100 @@ __global__ __launch_bounds__(256) void softmax_topk_kernel(const float* __restri
   }
 }
 
+// 16-lane reductions (DPP quad and row permutations only: every lane of a
+// group of 16 ends with the same result).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, dpp<kDppXor1>(v));
+  v = max(v, dpp<kDppXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));
+  return max(v, dpp<kDppMirror>(v));
+}
+__device__ __forceinline__ uint32_t row16_min_u32(uint32_t v) {
+  v = min(v, dpp<kDppXor1>(v));
+  v = min(v, dpp<kDppXor2>(v));
+  v = min(v, dpp<kDppHalfMirror>(v));
+  return min(v, dpp<kDppMirror>(v));
+}
+__device__ __forceinline__ float row16_sum_f32(float v) {
+  v += __builtin_bit_cast(float, dpp<kDppXor1>(__builtin_bit_cast(uint32_t, v)));
+  v += __builtin_bit_cast(float, dpp<kDppXor2>(__builtin_bit_cast(uint32_t, v)));
+  v += __builtin_bit_cast(float, dpp<kDppHalfMirror>(__builtin_bit_cast(uint32_t, v)));
+  return v + __builtin_bit_cast(float, dpp<kDppMirror>(__builtin_bit_cast(uint32_t, v)));
+}
+
+// E = 256, k <= 16: four rows per wave, 16 lanes per row. Lane j of a row
+// holds experts 64 c + 4 j + e (c, e = 0..3) in key[4 c + e], i.e. in
+// increasing expert order, so "strictly larger replaces" keeps the lowest
+// index among equal keys within the lane; across lanes the lowest index among
+// the holders of the row max is a 16-lane min. Lane j records rank j.
+__global__ __launch_bounds__(256) void softmax_topk_e256_kernel(const float* __restrict__ logits,
+                                                                int T, int k, int renorm,
+                                                                float* __restrict__ weights,
+                                                                int32_t* __restrict__ indices) {
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  // A row past T reads the last row (valid memory) and writes nothing; all 64
+  // lanes stay active for the DPP reductions.
+  const float* x = logits + (size_t)min(row, T - 1) * 256;
+
+  uint32_t key[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x) + 16 * c + j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[4 * c + e] = order_key(w[e]);
+  }
+
+  uint32_t taken = 0, top = 0, my_key = 0;
+  int my_idx = 0;
+  for (int r = 0; r < k; ++r) {
+    uint32_t bk = 0;
+    int bt = 0;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint32_t kt = ((taken >> t) & 1u) ? 0u : key[t];
+      if (kt > bk) {
+        bk = kt;
+        bt = t;
+      }
+    }
+    const uint32_t wk = row16_max_u32(bk);
+    const uint32_t mine = 64 * (bt >> 2) + 4 * j + (bt & 3);
+    const int widx = (int)row16_min_u32(bk == wk ? mine : 0xffffffffu);
+    if (((widx >> 2) & 15) == j) taken |= 1u << (4 * (widx >> 6) + (widx & 3));
+    if (r == 0) top = wk;
+    if (j == r) {
+      my_key = wk;
+      my_idx = widx;
+    }
+  }
+
+  const float m = key_value(top);
+  const float e = (j < k) ? expf(key_value(my_key) - m) : 0.f;
+  float denom;
+  if (renorm) {
+    denom = row16_sum_f32(e);
+  } else {
+    float l = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) l += fast_exp2((key_value(key[t]) - m) * kLog2e);
+    denom = row16_sum_f32(l);
+  }
+  if (row < T && j < k) {
+    weights[(size_t)row * k + j] = e / denom;
+    indices[(size_t)row * k + j] = my_idx;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_softmax_topk(const float* logits, int T, int E, int k, int renormalize,
                                float* weights, int32_t* indices, hipStream_t stream) {
+  if (E == 256 && k <= 16) {
+    hipLaunchKernelGGL(softmax_topk_e256_kernel, dim3((T + 15) / 16), dim3(256), 0, stream, logits,
+                       T, k, renormalize, weights, indices);
+    return hipGetLastError();
+  }
   dim3 grid((T + 3) / 4);
   const int nc = (E + 255) / 256;
   if (nc <= 1)

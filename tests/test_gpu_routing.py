@@ -29,7 +29,7 @@ def test_routing_config(renormalize):
     _check(inputs.routing_inputs(3, 16384, 256), 8, renormalize)
 
 
-@pytest.mark.parametrize("E,k", [(4, 1), (4, 4), (64, 2), (128, 8), (256, 32), (512, 8), (1024, 16), (1000, 5)])
+@pytest.mark.parametrize("E,k", [(4, 1), (4, 4), (64, 2), (128, 8), (256, 1), (256, 8), (256, 16), (256, 32), (512, 8), (1024, 16), (1000, 5)])
 def test_routing_shapes(E, k):
     print_case(test="routing_shapes", E=E, k=k)
     _check(inputs.routing_inputs(9, 37, E), k, True)
