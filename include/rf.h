@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 1
+#define RF_ABI_VERSION 2
 
 typedef enum {
   RF_OK = 0,
@@ -148,6 +148,28 @@ rf_status rf_absmax_quant_fp8(const void* x, int rows, int cols, uint8_t* q, flo
 rf_status rf_absmax_quant_gemm_fp8(const void* a, const uint8_t* b, const float* b_scale, int M,
                                    int N, int K, uint8_t* a_q, float* a_scale, void* c,
                                    hipStream_t stream);
+
+/*
+ * rf_absmax_quant_gemm_fp8_running -- the FP8 cascade as one pass with a running
+ * per-row scale (transcript cue 33, the loop as stated there): no abs-max pass
+ * over A first. K is walked in tiles of 64 columns; for tile t, row i's
+ * running abs-max a_i rises to include the tile, s_i = fp32(a_i / 448), the
+ * tile is quantised with that s_i exactly like rf_absmax_quant_fp8 quantises a
+ * row (correctly rounded fp32 x / s_i, round-to-nearest-even e4m3; codes 0
+ * while a_i = 0), and when s_i grew the running fp32 accumulator row is first
+ * multiplied by s_old / s_new. At the end C_ij = bf16(s_i * t_j * acc_ij).
+ * Early tiles are quantised with a smaller scale than the row's final one, so
+ * C differs from rf_absmax_quant_gemm_fp8 by the quantisation of those tiles.
+ *
+ *   a       [M, K] bf16
+ *   b       [N, K] uint8 e4m3 codes (K contiguous), b_scale [N] fp32
+ *   a_scale [M] fp32, written: the final scale (equal to rf_absmax_quant_fp8's)
+ *   c       [M, N] bf16
+ *   K % 128 == 0 and K <= 8192; M, N >= 0. No workspace.
+ */
+rf_status rf_absmax_quant_gemm_fp8_running(const void* a, const uint8_t* b, const float* b_scale,
+                                           int M, int N, int K, float* a_scale, void* c,
+                                           hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* rf_status_string(rf_status s);

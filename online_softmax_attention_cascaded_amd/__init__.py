@@ -13,10 +13,12 @@ from .binding import (  # noqa: F401
     attn_fwd,
     absmax_quant_fp8,
     absmax_quant_gemm_fp8,
+    absmax_quant_gemm_fp8_running,
     lib,
     merge_states,
     rf_absmax_quant_fp8,
     rf_absmax_quant_gemm_fp8,
+    rf_absmax_quant_gemm_fp8_running,
     rf_attn_decode_split,
     rf_attn_fwd,
     rf_merge_states,

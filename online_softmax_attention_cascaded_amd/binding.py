@@ -30,6 +30,7 @@ SIGNATURES = {
     "rf_softmax_topk": [_P, _I, _I, _I, _I, _P, _P, _P],
     "rf_absmax_quant_fp8": [_P, _I, _I, _P, _P, _P],
     "rf_absmax_quant_gemm_fp8": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
+    "rf_absmax_quant_gemm_fp8_running": [_P, _P, _P, _I, _I, _I, _P, _P, _P],
     "rf_status_string": [_I],
     "rf_last_error": [],
     "rf_abi_version": [],
@@ -147,6 +148,14 @@ def rf_absmax_quant_gemm_fp8(a, b_q, b_scale, a_q, a_scale, c):
                                           _ptr(a_scale), _ptr(c), _stream(a)))
 
 
+def rf_absmax_quant_gemm_fp8_running(a, b_q, b_scale, a_scale, c):
+    _dev(a, b_q, b_scale, a_scale, c)
+    M, K = a.shape
+    N = b_q.shape[0]
+    _check(lib().rf_absmax_quant_gemm_fp8_running(_ptr(a), _ptr(b_q), _ptr(b_scale), M, N, K,
+                                                  _ptr(a_scale), _ptr(c), _stream(a)))
+
+
 # ---------------------------------------------------------------- allocating helpers
 
 
@@ -203,3 +212,13 @@ def absmax_quant_gemm_fp8(a, b_q, b_scale):
     c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     rf_absmax_quant_gemm_fp8(a, b_q, b_scale, a_q, a_scale, c)
     return c, a_q, a_scale
+
+
+def absmax_quant_gemm_fp8_running(a, b_q, b_scale):
+    """One-pass FP8 GEMM with a running per-row scale; returns (c, a_scale)."""
+    M, K = a.shape
+    N = b_q.shape[0]
+    a_scale = torch.empty(M, dtype=torch.float32, device=a.device)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    rf_absmax_quant_gemm_fp8_running(a, b_q, b_scale, a_scale, c)
+    return c, a_scale

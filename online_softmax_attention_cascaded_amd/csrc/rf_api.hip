@@ -163,6 +163,24 @@ rf_status rf_absmax_quant_gemm_fp8(const void* a, const uint8_t* b, const float*
                      "rf_absmax_quant_gemm_fp8 (gemm)");
 }
 
+rf_status rf_absmax_quant_gemm_fp8_running(const void* a, const uint8_t* b, const float* b_scale,
+                                           int M, int N, int K, float* a_scale, void* c,
+                                           hipStream_t stream) {
+  RF_REQUIRE(M >= 0 && N >= 0 && K >= 0, RF_ERR_INVALID_ARG,
+             "rf_absmax_quant_gemm_fp8_running: negative size");
+  if ((long long)M * N == 0) return ok();
+  RF_REQUIRE(K >= 128 && K % 128 == 0, RF_ERR_INVALID_ARG,
+             "rf_absmax_quant_gemm_fp8_running: K=%d must be a positive multiple of 128", K);
+  RF_REQUIRE(K <= 8192, RF_ERR_UNSUPPORTED, "rf_absmax_quant_gemm_fp8_running: K=%d > 8192", K);
+  RF_REQUIRE(a && b && b_scale && a_scale && c, RF_ERR_INVALID_ARG,
+             "rf_absmax_quant_gemm_fp8_running: null tensor pointer");
+  RF_REQUIRE(aligned(a, 16) && aligned(b, 16) && aligned(c, 4) && aligned(b_scale, 4) &&
+                 aligned(a_scale, 4),
+             RF_ERR_INVALID_ARG, "rf_absmax_quant_gemm_fp8_running: misaligned pointer");
+  return from_launch(rf::launch_gemm_fp8_running(a, b, b_scale, M, N, K, a_scale, c, stream),
+                     "rf_absmax_quant_gemm_fp8_running");
+}
+
 const char* rf_status_string(rf_status s) {
   switch (s) {
     case RF_OK: return "RF_OK";

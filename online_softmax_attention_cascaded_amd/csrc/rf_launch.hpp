@@ -34,4 +34,7 @@ hipError_t launch_gemm_fp8_scaled(const uint8_t* a_q, const float* a_scale, cons
                                   const float* b_scale, int M, int N, int K, void* c,
                                   hipStream_t stream);
 
+hipError_t launch_gemm_fp8_running(const void* a, const uint8_t* b_q, const float* b_scale, int M,
+                                   int N, int K, float* a_scale, void* c, hipStream_t stream);
+
 }  // namespace rf

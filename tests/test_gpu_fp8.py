@@ -107,3 +107,67 @@ def test_fp8_config_sampled():
     assert np.array_equal(bq[:512].cpu().numpy(), bq_ref)
     c_ref = oracle.quant_gemm(aq_ref, sa_ref, bq.cpu().numpy(), bs.cpu().numpy())
     assert rel_fro(np32(c)[rows], c_ref) <= FP8_REL_FRO
+
+
+# ---- one-pass form with a running per-row scale (K tiles of 64 columns)
+
+K_TILE = 64
+
+
+def _running_case(a, bsrc):
+    bq, bs = rf.absmax_quant_fp8(bsrc.to(DEV))
+    c, sa = rf.absmax_quant_gemm_fp8_running(a.to(DEV), bq, bs)
+    x = a.float().numpy()
+    c_ref = oracle.quant_gemm_running_scale(x, bq.cpu().numpy(), bs.cpu().numpy(), K_TILE)
+    _, sa_ref = oracle.absmax_quant(x)
+    return np32(c), c_ref, sa.cpu().numpy(), sa_ref, bq, bs
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 256), (300, 200, 512), (256, 512, 1024), (1, 3, 128),
+                                   (513, 260, 7168)])
+def test_running_scale_gemm_small(M, N, K):
+    print_case(test="gemm_running", M=M, N=N, K=K)
+    a, bsrc = inputs.quant_inputs(12, M, N, K)
+    c, c_ref, sa, sa_ref, _, _ = _running_case(a, bsrc)
+    assert np.array_equal(sa, sa_ref)          # the final running scale is the row's scale
+    assert rel_fro(c, c_ref) <= 5e-3
+
+
+def test_running_scale_growth_and_zero_rows():
+    """Rows whose abs-max grows late (an outlier in the last K tile), rows that
+    start with zero tiles, and an all-zero row."""
+    M, N, K = 96, 128, 1024
+    a, bsrc = inputs.quant_inputs(13, M, N, K)
+    a = a.clone()
+    a[1, :] = 0
+    a[2, : K // 2] = 0
+    a[3, -1] = 1000.0
+    a[4, 5 * K_TILE + 3] = -300.0
+    print_case(test="gemm_running_growth")
+    c, c_ref, sa, sa_ref, _, _ = _running_case(a, bsrc)
+    assert np.array_equal(sa, sa_ref)
+    assert np.all(c[1] == 0)
+    assert rel_fro(c, c_ref) <= 5e-3
+    for r in (2, 3, 4):
+        assert rel_fro(c[r], c_ref[r]) <= 5e-3
+
+
+def test_running_scale_config_sampled():
+    """M=4096, N=4096, K=7168 with the FP8 workload's outliers: 64 sampled rows
+    against the one-pass oracle; the deviation from the final-scale path is the
+    quantisation of the early K tiles (reported, not gated beyond 3e-2)."""
+    print_case(test="gemm_running_full")
+    M, N, K = 4096, 4096, 7168
+    a, bsrc = inputs.quant_inputs(4, M, N, K)
+    bq, bs = rf.absmax_quant_fp8(bsrc.to(DEV))
+    c, sa = rf.absmax_quant_gemm_fp8_running(a.to(DEV), bq, bs)
+    rows = np.random.default_rng(1).choice(M, 64, replace=False)
+    x = a[rows].float().numpy()
+    c_ref = oracle.quant_gemm_running_scale(x, bq.cpu().numpy(), bs.cpu().numpy(), K_TILE)
+    assert rel_fro(np32(c)[rows], c_ref) <= 5e-3
+    aq_f, sa_f = oracle.absmax_quant(x)
+    assert np.array_equal(sa.cpu().numpy()[rows], sa_f)
+    c_final = oracle.quant_gemm(aq_f, sa_f, bq.cpu().numpy(), bs.cpu().numpy())
+    dev_final = rel_fro(c_ref, c_final)
+    print(f"running-scale vs final-scale quantisation: {dev_final:.4f} relative Frobenius")
+    assert dev_final <= FP8_REL_FRO

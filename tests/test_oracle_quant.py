@@ -155,6 +155,22 @@ def test_running_scale_single_tile_is_the_final_scale_path():
     assert np.allclose(c1, c2, rtol=1e-15, atol=0)
 
 
+def test_running_scale_growth_worked_case():
+    """Transcript cue 33 with a scale that grows between two K tiles, by hand:
+    tile 1 = [1, 0.5] (abs-max 1), tile 2 = [4, -2] (abs-max 4), B = ones with
+    column scale 1. Tile 1 is quantised with s1 = 1/448 (codes 448, 224), the
+    accumulator (672) is multiplied by s1/s2 = 1/4 when tile 2 raises the scale
+    to s2 = 4/448, tile 2 adds 448 - 224; the final scale gives
+    s2 * (168 + 224) = 3.5 = 1 + 0.5 + 4 - 2. (B's codes decode to 448 with
+    column scale 1/448.) A wrong rescale direction gives s2 * (2688 + 224), a
+    missing rescale s2 * 896."""
+    x = np.array([[1.0, 0.5, 4.0, -2.0]], np.float32)
+    bq, sb = oracle.absmax_quant(np.ones((1, 4), np.float32))
+    assert sb[0] == np.float32(1.0 / 448.0) and np.all(e4m3_decode(bq) == 448.0)
+    c = oracle.quant_gemm_running_scale(x, bq, sb, 2)
+    assert abs(c[0, 0] - 3.5) <= 1e-6
+
+
 def test_outlier_generator():
     a, _ = inputs.quant_inputs(7, 100, 2, 1000)
     x = a.float().numpy()
