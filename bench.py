@@ -315,6 +315,25 @@ def main():
         },
     }
     progress(f"timed {args.steps} steps in {wall:.2f} s")
+
+    # The one-pass running-scale FP8 GEMM (quantises A inside the K loop) is
+    # an alternative to the step's quantise + GEMM, timed on its own.
+    sr = torch.empty(F["M"], device=dev)
+    for i in range(10):
+        rf.rf_absmax_quant_gemm_fp8_running(a_bufs[i % FP8_ROTATE], bq, bs, sr, c)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        rf.rf_absmax_quant_gemm_fp8_running(a_bufs[i % FP8_ROTATE], bq, bs, sr, c)
+    e1.record()
+    torch.cuda.synchronize()
+    t_run = e0.elapsed_time(e1) / 1e3 / args.steps
+    result["us_per_launch"]["fp8_running"] = round(t_run * 1e6, 2)
+    result["rooflines"]["fp8_running_scale_one_pass"] = {
+        "bound": "mfma", "achieved": round(gemm_flops() / t_run / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(gemm_flops() / t_run / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "note": "single kernel: running per-row scale, A quantised inside the K loop"}
     if not args.no_cpu_baseline:
         progress("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline()
