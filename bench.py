@@ -7,6 +7,9 @@ seeded input already resident in HBM:
     partial states + merge;
   MoE routing, 16384 x 256 fp32 logits, softmax -> top-8 (renormalised);
   FP8 per-token quantise + GEMM, M=N=4096, K=7168.
+After the timed steps, two alternatives are timed on their own: the one-pass
+running-scale FP8 GEMM, and safe softmax over rows of 1K..8K fp32 values at
+each fusion level of the reduction tree (unfused, thread, wave, block).
 Routing logits rotate over 20 buffers and the FP8 A operand over 5, so those
 inputs (which would otherwise fit the 256 MB last-level cache) come from HBM.
 
@@ -34,6 +37,8 @@ PREFILL = dict(B=4, H=32, L=2048, d=128)
 DECODE = dict(B=8, Hq=32, Hkv=8, Lk=32768, d=128)
 ROUTING = dict(T=16384, E=256, k=8)
 FP8 = dict(M=4096, N=4096, K=7168)
+SOFTMAX_VALUES = 1 << 26
+SOFTMAX_E = (1024, 2048, 4096, 8192)
 DECODE_SEGMENTS = (4, 16, 64)
 ROUTING_ROTATE = 20
 FP8_ROTATE = 5
@@ -334,6 +339,42 @@ def main():
         "bound": "mfma", "achieved": round(gemm_flops() / t_run / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
         "unit": "TFLOP/s", "frac": round(gemm_flops() / t_run / 1e12 / PEAK_FP8_TFLOPS, 4),
         "note": "single kernel: running per-row scale, A quantised inside the K loop"}
+    # Safe softmax alone at each fusion level of the reduction tree, rows of
+    # 1K .. 8K fp32 values, 2^26 values per launch. The rate is counted with the
+    # fused form's algorithmic bytes (x read once, y written once: 8 B/value)
+    # for every level, so the rates compare like for like; the unfused cascade
+    # moves 16 B/value (three reads of x, one write).
+    levels = {"unfused": rf.RF_FUSE_NONE, "thread": rf.RF_FUSE_THREAD, "wave": rf.RF_FUSE_WAVE,
+              "block": rf.RF_FUSE_BLOCK}
+    sm_rates = {}
+    for E in SOFTMAX_E:
+        T = SOFTMAX_VALUES // E
+        xs = inputs.softmax_inputs(6, T, E).to(dev)
+        ys = torch.empty_like(xs)
+        work = torch.empty(2 * T, device=dev)
+        for lname, lv in levels.items():
+            for _ in range(10):
+                rf.rf_softmax(xs, lv, work, ys)
+            e0.record()
+            for _ in range(args.steps):
+                rf.rf_softmax(xs, lv, work, ys)
+            e1.record()
+            torch.cuda.synchronize()
+            t_sm = e0.elapsed_time(e1) / 1e3 / args.steps
+            sm_rates[(E, lname)] = (t_sm, 8.0 * T * E / t_sm / 1e9)
+        del xs, ys, work
+    result["softmax_fusion_levels"] = {
+        "values_per_launch": SOFTMAX_VALUES,
+        "unit": "GB/s at 8 B/value (x read once, y written once)",
+        "us_per_launch": {f"E{E}": {ln: round(sm_rates[(E, ln)][0] * 1e6, 2) for ln in levels}
+                          for E in SOFTMAX_E},
+        "GBs": {f"E{E}": {ln: round(sm_rates[(E, ln)][1], 1) for ln in levels} for E in SOFTMAX_E},
+    }
+    best_sm = max(sm_rates[(E, "block")][1] for E in SOFTMAX_E)
+    result["rooflines"]["softmax_block_level"] = {
+        "bound": "hbm", "achieved": round(best_sm, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": round(best_sm / PEAK_HBM_GBS, 4), "note": "best row length of the block-level form"}
+    progress("softmax fusion levels timed")
     if not args.no_cpu_baseline:
         progress("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline()

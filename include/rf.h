@@ -15,6 +15,8 @@
  *     and "Single-Segment vs Multi-Segment");
  *   - MoE routing: softmax followed by top-k (transcript cue 11;
  *     "Online normalizer calculation for softmax", abstract);
+ *   - safe softmax alone, fused at the thread, wave or workgroup level of the
+ *     reduction tree (transcript cue 47);
  *   - FP8: per-token abs-max, scale, e4m3 cast, then GEMM (transcript cue 33).
  *
  * Conventions for every entry point:
@@ -42,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 2
+#define RF_ABI_VERSION 3
 
 typedef enum {
   RF_OK = 0,
@@ -117,6 +119,30 @@ rf_status rf_merge_states(const float* part_m, const float* part_l, const float*
  */
 rf_status rf_softmax_topk(const float* logits, int T, int E, int k, int renormalize,
                           float* weights, int32_t* indices, hipStream_t stream);
+
+/* Where rf_softmax updates its running (m, l) state in the reduction tree. */
+enum {
+  RF_FUSE_NONE = 0,   /* unfused cascade: max kernel, sum kernel, divide kernel */
+  RF_FUSE_THREAD = 1, /* per value, in each thread; thread states merged after */
+  RF_FUSE_WAVE = 2,   /* per 256-value wave segment; wave states merged after */
+  RF_FUSE_BLOCK = 3   /* per 1024-value workgroup tile */
+};
+
+/*
+ * rf_softmax -- safe softmax of each row, y_ij = exp(x_ij - m_i) / l_i with
+ * m_i = max_j x_ij and l_i = sum_j exp(x_ij - m_i), with the max -> sum
+ * cascade fused at the chosen level of the reduction tree (transcript cue 47:
+ * fusion levels on safe softmax of 1K to 8K values; cue 17: the running state
+ * rescaled by exp(m_old - m_new) when the max grows). Every fused level reads
+ * x once; RF_FUSE_NONE reads it three times and keeps m and l in `work`.
+ *
+ *   x [T, E] fp32;  y [T, E] fp32;  4 <= E <= 8192, E % 4 == 0.
+ *   work  [2 * T] fp32 caller-owned scratch, 4-byte aligned, used (and
+ *         overwritten) only by RF_FUSE_NONE; may be NULL otherwise.
+ *   Rows are expected to hold at least one finite value.
+ */
+rf_status rf_softmax(const float* x, int T, int E, int level, float* work, float* y,
+                     hipStream_t stream);
 
 /*
  * rf_absmax_quant_fp8 -- per-row abs-max, scale and e4m3 cast (transcript

@@ -7,6 +7,10 @@ library; the first call does, and raises if it has not been built.
 """
 
 from .binding import (  # noqa: F401
+    RF_FUSE_BLOCK,
+    RF_FUSE_NONE,
+    RF_FUSE_THREAD,
+    RF_FUSE_WAVE,
     RFError,
     attn_decode,
     attn_decode_partials,
@@ -22,6 +26,8 @@ from .binding import (  # noqa: F401
     rf_attn_decode_split,
     rf_attn_fwd,
     rf_merge_states,
+    rf_softmax,
     rf_softmax_topk,
+    softmax,
     softmax_topk,
 )

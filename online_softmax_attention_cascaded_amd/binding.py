@@ -18,6 +18,7 @@ from .build import LIB_PATH
 
 RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_LAUNCH = 0, 1, 2, 3
 RF_F32, RF_BF16 = 0, 1
+RF_FUSE_NONE, RF_FUSE_THREAD, RF_FUSE_WAVE, RF_FUSE_BLOCK = 0, 1, 2, 3
 
 # Every entry point of the C ABI with its argument types.
 _P = ctypes.c_void_p
@@ -28,6 +29,7 @@ SIGNATURES = {
     "rf_attn_decode_split": [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
     "rf_merge_states": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
     "rf_softmax_topk": [_P, _I, _I, _I, _I, _P, _P, _P],
+    "rf_softmax": [_P, _I, _I, _I, _P, _P, _P],
     "rf_absmax_quant_fp8": [_P, _I, _I, _P, _P, _P],
     "rf_absmax_quant_gemm_fp8": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
     "rf_absmax_quant_gemm_fp8_running": [_P, _P, _P, _I, _I, _I, _P, _P, _P],
@@ -134,6 +136,14 @@ def rf_softmax_topk(logits, k, renormalize, weights, indices):
                                  _ptr(indices), _stream(logits)))
 
 
+def rf_softmax(x, level, work, y):
+    _dev(x, work, y)
+    if x.dtype != torch.float32 or y.dtype != torch.float32:
+        raise ValueError("rf_softmax takes fp32 x and y")
+    T, E = x.shape
+    _check(lib().rf_softmax(_ptr(x), T, E, int(level), _ptr(work), _ptr(y), _stream(x)))
+
+
 def rf_absmax_quant_fp8(x, q, scale):
     _dev(x, q, scale)
     rows, cols = x.shape
@@ -195,6 +205,14 @@ def softmax_topk(logits, k, renormalize=True):
     idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     rf_softmax_topk(logits, k, renormalize, w, idx)
     return w, idx
+
+
+def softmax(x, level=RF_FUSE_BLOCK):
+    """Row softmax of fp32 x [T, E] with the cascade fused at ``level``."""
+    y = torch.empty_like(x)
+    work = torch.empty(2 * x.shape[0], dtype=torch.float32, device=x.device) if level == RF_FUSE_NONE else None
+    rf_softmax(x, level, work, y)
+    return y
 
 
 def absmax_quant_fp8(x):

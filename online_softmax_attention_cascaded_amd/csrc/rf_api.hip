@@ -132,6 +132,23 @@ rf_status rf_softmax_topk(const float* logits, int T, int E, int k, int renormal
                      "rf_softmax_topk");
 }
 
+rf_status rf_softmax(const float* x, int T, int E, int level, float* work, float* y,
+                     hipStream_t stream) {
+  RF_REQUIRE(T >= 0 && E >= 0, RF_ERR_INVALID_ARG, "rf_softmax: negative size");
+  RF_REQUIRE(level >= RF_FUSE_NONE && level <= RF_FUSE_BLOCK, RF_ERR_INVALID_ARG,
+             "rf_softmax: unknown fusion level %d", level);
+  if (T == 0) return ok();
+  RF_REQUIRE(E >= 4 && E % 4 == 0, RF_ERR_INVALID_ARG, "rf_softmax: E=%d must be a positive multiple of 4", E);
+  RF_REQUIRE(E <= 8192, RF_ERR_UNSUPPORTED, "rf_softmax: E=%d > 8192", E);
+  RF_REQUIRE(x && y, RF_ERR_INVALID_ARG, "rf_softmax: null tensor pointer");
+  RF_REQUIRE(level != RF_FUSE_NONE || work, RF_ERR_INVALID_ARG,
+             "rf_softmax: the unfused cascade needs a workspace of 2*T floats");
+  RF_REQUIRE(aligned(x, 16) && aligned(y, 16) && aligned(work, 4), RF_ERR_INVALID_ARG,
+             "rf_softmax: misaligned pointer");
+  RF_REQUIRE((long long)T * E < (1LL << 40), RF_ERR_INVALID_ARG, "rf_softmax: problem too large");
+  return from_launch(rf::launch_softmax_rows(x, T, E, level, work, y, stream), "rf_softmax");
+}
+
 rf_status rf_absmax_quant_fp8(const void* x, int rows, int cols, uint8_t* q, float* scale,
                               hipStream_t stream) {
   RF_REQUIRE(rows >= 0 && cols >= 0, RF_ERR_INVALID_ARG, "rf_absmax_quant_fp8: negative size");

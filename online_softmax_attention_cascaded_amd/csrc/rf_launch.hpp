@@ -27,6 +27,9 @@ hipError_t launch_merge_states(const float* part_m, const float* part_l, const f
 hipError_t launch_softmax_topk(const float* logits, int T, int E, int k, int renormalize,
                                float* weights, int32_t* indices, hipStream_t stream);
 
+hipError_t launch_softmax_rows(const float* x, int T, int E, int level, float* work, float* y,
+                               hipStream_t stream);
+
 hipError_t launch_absmax_quant_fp8(const void* x, int rows, int cols, uint8_t* q, float* scale,
                                    hipStream_t stream);
 

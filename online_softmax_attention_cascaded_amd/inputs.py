@@ -15,6 +15,7 @@ pages do not print):
 * decode: B=8, Hq=32, Hkv=8, Lk=32768, d=128, bf16 KV cache;
 * routing: 16384 tokens x 256 experts fp32 logits, 1 % of rows with +6 on one
   random expert;
+* safe softmax: rows of 1024 .. 8192 fp32 values, 2^26 values in all;
 * FP8: A 4096 x 7168 bf16 with 0.1 % of entries scaled by 50, B source
   4096 x 7168 bf16 (quantised per row of B, i.e. per output column).
 """
@@ -75,6 +76,19 @@ def routing_inputs(seed, T, E, spike_frac=0.01, spike=6.0):
     rows = rng.choice(T, size=n, replace=False)
     cols = rng.integers(0, E, size=n)
     x[rows, cols] += np.float32(spike)
+    return torch.from_numpy(x)
+
+
+def softmax_inputs(seed, T, E, sigma=4.0, ramp=8.0):
+    """fp32 rows [T, E] ~ sigma * N(0,1); row i with i % 4 == 1 also gets a
+    ramp rising linearly from 0 to ``ramp`` along the row (its running max keeps
+    growing, so every tile rescales the state), and i % 4 == 2 the same ramp
+    falling (the max is met early)."""
+    rng = np.random.default_rng(seed)
+    x = normal(rng, (T, E)) * np.float32(sigma)
+    r = np.linspace(0.0, ramp, E, dtype=np.float32)
+    x[1::4] += r
+    x[2::4] += r[::-1]
     return torch.from_numpy(x)
 
 

@@ -55,7 +55,7 @@ def test_argument_counts_match_header():
 
 
 def test_status_helpers(lib):
-    assert lib.rf_abi_version() == 2
+    assert lib.rf_abi_version() == 3
     assert lib.rf_status_string(OK) == b"RF_OK"
     assert lib.rf_status_string(INVALID) == b"RF_ERR_INVALID_ARG"
     assert lib.rf_status_string(UNSUPPORTED) == b"RF_ERR_UNSUPPORTED"
@@ -139,6 +139,20 @@ def test_topk_validation(lib):
     assert f(FAKE, 10, 256, 40, 1, FAKE, FAKE, None) == UNSUPPORTED
     assert f(MISALIGNED, 10, 256, 8, 1, FAKE, FAKE, None) == INVALID
     assert f(None, 0, 256, 8, 1, None, None, None) == OK
+
+
+def test_softmax_validation(lib):
+    f = lib.rf_softmax
+    assert f(FAKE, 10, 1024, 4, None, FAKE, None) == INVALID      # unknown level
+    assert f(FAKE, -1, 1024, 3, None, FAKE, None) == INVALID
+    assert f(FAKE, 10, 1022, 3, None, FAKE, None) == INVALID      # E % 4
+    assert f(FAKE, 10, 0, 3, None, FAKE, None) == INVALID
+    assert f(FAKE, 10, 8196, 3, None, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 10, 1024, 0, None, FAKE, None) == INVALID      # unfused needs work
+    assert f(MISALIGNED, 10, 1024, 2, None, FAKE, None) == INVALID
+    assert f(FAKE, 10, 1024, 1, None, None, None) == INVALID
+    assert f(None, 0, 1024, 0, None, None, None) == OK
+    assert lib.rf_last_error() == b""
 
 
 def test_quant_validation(lib):

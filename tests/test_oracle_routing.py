@@ -43,6 +43,19 @@ def test_softmax_matches_torch_float64():
     assert np.allclose(p.sum(axis=1), 1.0, atol=1e-14)
 
 
+def test_softmax_closed_form_and_safety():
+    """exp(ln j) = j: the row [0, ln 2, ln 3, ln 4] has softmax [1, 2, 3, 4] / 10,
+    whatever constant is added (even +-1000, where exp alone over- or
+    underflows); a constant row is uniform; -inf entries get weight 0."""
+    base = np.log(np.array([1.0, 2.0, 3.0, 4.0]))
+    want = np.array([1.0, 2.0, 3.0, 4.0]) / 10.0
+    for c in (0.0, 1000.0, -1000.0, 37.5):
+        assert np.allclose(oracle.softmax_rows((base + c)[None]), want, rtol=1e-12, atol=0)
+    assert np.all(oracle.softmax_rows(np.full((2, 7), -3.25)) == 1.0 / 7)
+    p = oracle.softmax_rows(np.array([[0.0, -np.inf, np.log(3.0), -np.inf]]))
+    assert np.allclose(p, [[0.25, 0.0, 0.75, 0.0]], rtol=1e-15, atol=0)
+
+
 def test_weights_invariants_and_modes():
     x = inputs.routing_inputs(3, 64, 256).numpy()
     w, idx = oracle.softmax_topk(x, 8, renormalize=True)
