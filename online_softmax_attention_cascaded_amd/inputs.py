@@ -16,6 +16,8 @@ pages do not print):
 * routing: 16384 tokens x 256 experts fp32 logits, 1 % of rows with +6 on one
   random expert;
 * safe softmax: rows of 1024 .. 8192 fp32 values, 2^26 values in all;
+* variance / moment of inertia: rows of 1024 .. 8192 fp32 positions and
+  masses, 2^26 values in all;
 * FP8: A 4096 x 7168 bf16 with 0.1 % of entries scaled by 50, B source
   4096 x 7168 bf16 (quantised per row of B, i.e. per output column).
 """
@@ -90,6 +92,20 @@ def softmax_inputs(seed, T, E, sigma=4.0, ramp=8.0):
     x[1::4] += r
     x[2::4] += r[::-1]
     return torch.from_numpy(x)
+
+
+def moment_inputs(seed, T, E, offsets=(0.0, 1000.0, -50.0, 3.0), scales=(1.0, 0.01, 10.0, 1.0)):
+    """Positions x [T, E] fp32: row i is offsets[i % 4] + scales[i % 4] * N(0,1)
+    (mean-to-spread ratios up to 1e5, where the one-pass sum of squares minus
+    the squared sum loses every digit in fp32); masses w [T, E] fp32 uniform on
+    [0, 1)."""
+    rng = np.random.default_rng(seed)
+    x = normal(rng, (T, E))
+    off = np.asarray(offsets, np.float32)[np.arange(T) % len(offsets)][:, None]
+    sc = np.asarray(scales, np.float32)[np.arange(T) % len(scales)][:, None]
+    x = (x * sc + off).astype(np.float32)
+    w = rng.random((T, E), dtype=np.float32)
+    return torch.from_numpy(x), torch.from_numpy(w)
 
 
 def tie_heavy_logits(seed, T, E, values=(-1.0, 0.0, 1.0, 2.0)):

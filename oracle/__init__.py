@@ -8,11 +8,12 @@ no kernels, headers, helpers or constant tables. The only code both sides meet
 is the seeded input generator, which holds none of the method's arithmetic.
 
 Every result here is written as the *unfused* cascade the pages describe
-(max, then sum of exponentials, then divide, then multiply), in float64 with
+(max, then sum of exponentials, then divide, then multiply; mean, then the
+centred second moment), in float64 with
 numpy, so a reader can check it against the pages by eye. Sources:
 
 * "RedFuser episode transcript" (podcast.do-not-panic.com, episode of
-  2026-10-13), cues 5, 9, 11, 15, 19, 21, 29, 31, 33, 39.
+  2026-10-13), cues 5, 9, 11, 15, 19, 21, 29, 31, 33, 39, 47.
 * "RedFuser episode visual explainer" (same site, /viz/), the widgets
   "Online softmax, step by step", "Rescale the output accumulator too" and
   "Merging partial states across blocks (FlashDecoding-style)".
@@ -34,6 +35,7 @@ from .attention import (
 from .routing import softmax_rows, softmax_topk
 from .codec import e4m3_decode, e4m3_encode, e4m3_table
 from .quant import absmax_quant, quant_gemm, quant_gemm_running_scale
+from .moments import row_inertia, row_variance
 
 __all__ = [
     "attention",
@@ -49,4 +51,6 @@ __all__ = [
     "absmax_quant",
     "quant_gemm",
     "quant_gemm_running_scale",
+    "row_inertia",
+    "row_variance",
 ]
