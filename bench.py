@@ -8,8 +8,9 @@ seeded input already resident in HBM:
   MoE routing, 16384 x 256 fp32 logits, softmax -> top-8 (renormalised);
   FP8 per-token quantise + GEMM, M=N=4096, K=7168.
 After the timed steps, two alternatives are timed on their own: the one-pass
-running-scale FP8 GEMM, and safe softmax over rows of 1K..8K fp32 values at
-each fusion level of the reduction tree (unfused, thread, wave, block).
+running-scale FP8 GEMM, and safe softmax, variance and moment of inertia over
+rows of 1K..8K fp32 values at each fusion level of the reduction tree
+(unfused, thread, wave, block).
 Routing logits rotate over 20 buffers and the FP8 A operand over 5, so those
 inputs (which would otherwise fit the 256 MB last-level cache) come from HBM.
 
@@ -375,6 +376,49 @@ def main():
         "bound": "hbm", "achieved": round(best_sm, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
         "frac": round(best_sm / PEAK_HBM_GBS, 4), "note": "best row length of the block-level form"}
     progress("softmax fusion levels timed")
+
+    # Variance and moment of inertia (centre, then centred second moment) at
+    # each fusion level, rows of 1K .. 8K values, 2^26 values per launch.
+    # Algorithmic bytes: 4 B/value (x) for the variance, 8 B/value (x and the
+    # masses) for the moment of inertia; the unfused cascade reads them twice.
+    mom = {}
+    for E in SOFTMAX_E:
+        T = SOFTMAX_VALUES // E
+        xm, wm = (t.to(dev) for t in inputs.moment_inputs(8, T, E))
+        oc = torch.empty(T, device=dev)
+        oi = torch.empty(T, device=dev)
+        for kind, per_value in (("variance", 4), ("inertia", 8)):
+            for lname, lv in levels.items():
+                def call():
+                    if kind == "variance":
+                        rf.rf_row_variance(xm, lv, oc, oi)
+                    else:
+                        rf.rf_row_inertia(xm, wm, lv, oc, oi)
+                for _ in range(10):
+                    call()
+                e0.record()
+                for _ in range(args.steps):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
+                t_m = e0.elapsed_time(e1) / 1e3 / args.steps
+                mom[(kind, E, lname)] = (t_m, per_value * T * E / t_m / 1e9)
+        del xm, wm, oc, oi
+    result["moment_fusion_levels"] = {
+        kind: {
+            "unit": f"GB/s at {per_value} B/value",
+            "us_per_launch": {f"E{E}": {ln: round(mom[(kind, E, ln)][0] * 1e6, 2) for ln in levels}
+                              for E in SOFTMAX_E},
+            "GBs": {f"E{E}": {ln: round(mom[(kind, E, ln)][1], 1) for ln in levels} for E in SOFTMAX_E},
+        }
+        for kind, per_value in (("variance", 4), ("inertia", 8))
+    }
+    for kind in ("variance", "inertia"):
+        best = max(mom[(kind, E, ln)][1] for E in SOFTMAX_E for ln in levels if ln != "unfused")
+        result["rooflines"][f"{kind}_fused_best"] = {
+            "bound": "hbm", "achieved": round(best, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(best / PEAK_HBM_GBS, 4)}
+    progress("variance and moment-of-inertia fusion levels timed")
     if not args.no_cpu_baseline:
         progress("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline()

@@ -17,6 +17,8 @@
  *     "Online normalizer calculation for softmax", abstract);
  *   - safe softmax alone, fused at the thread, wave or workgroup level of the
  *     reduction tree (transcript cue 47);
+ *   - variance and moment of inertia: a centre, then the centred second
+ *     moment, at the same fusion levels (transcript cue 47);
  *   - FP8: per-token abs-max, scale, e4m3 cast, then GEMM (transcript cue 33).
  *
  * Conventions for every entry point:
@@ -44,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 3
+#define RF_ABI_VERSION 4
 
 typedef enum {
   RF_OK = 0,
@@ -120,7 +122,8 @@ rf_status rf_merge_states(const float* part_m, const float* part_l, const float*
 rf_status rf_softmax_topk(const float* logits, int T, int E, int k, int renormalize,
                           float* weights, int32_t* indices, hipStream_t stream);
 
-/* Where rf_softmax updates its running (m, l) state in the reduction tree. */
+/* Where rf_softmax, rf_row_variance and rf_row_inertia update their running
+ * state in the reduction tree. */
 enum {
   RF_FUSE_NONE = 0,   /* unfused cascade: max kernel, sum kernel, divide kernel */
   RF_FUSE_THREAD = 1, /* per value, in each thread; thread states merged after */
@@ -143,6 +146,38 @@ enum {
  */
 rf_status rf_softmax(const float* x, int T, int E, int level, float* work, float* y,
                      hipStream_t stream);
+
+/*
+ * rf_row_variance -- per row, the mean mu_i = (1/E) sum_j x_ij and the
+ * population variance (1/E) sum_j (x_ij - mu_i)^2 (transcript cue 47 names
+ * the variance cascade: a mean, then the centred second moment). `level`
+ * (RF_FUSE_*) is where the running state (count, mean, centred sum) is
+ * updated; each step moves the mean and corrects the centred sum of the
+ * earlier values by count * (mean_old - mean_new)^2 (cue 17: correct for the
+ * changed earlier result, then add the tile's term). Fused levels read x once;
+ * RF_FUSE_NONE runs a mean pass and a centred pass. Positions are summed
+ * relative to each row's first value, so rows with a mean far above their
+ * spread keep their digits.
+ *
+ *   x [T, E] fp32 (16-byte aligned);  mean [T], var [T] fp32.
+ *   4 <= E <= 8192, E % 4 == 0. No workspace.
+ */
+rf_status rf_row_variance(const float* x, int T, int E, int level, float* mean, float* var,
+                          hipStream_t stream);
+
+/*
+ * rf_row_inertia -- per row of point masses w_ij >= 0 at positions x_ij on a
+ * line, the centre of mass c_i = sum_j w_ij x_ij / sum_j w_ij and the moment
+ * of inertia about it, I_i = sum_j w_ij (x_ij - c_i)^2 (transcript cue 47
+ * names the moment-of-inertia cascade). Fusion levels and the incremental step
+ * as in rf_row_variance, with masses in place of counts. A row whose masses
+ * sum to 0 gets centre NaN and inertia 0.
+ *
+ *   x, w [T, E] fp32 (16-byte aligned);  centre [T], inertia [T] fp32.
+ *   4 <= E <= 8192, E % 4 == 0. No workspace.
+ */
+rf_status rf_row_inertia(const float* x, const float* w, int T, int E, int level, float* centre,
+                         float* inertia, hipStream_t stream);
 
 /*
  * rf_absmax_quant_fp8 -- per-row abs-max, scale and e4m3 cast (transcript

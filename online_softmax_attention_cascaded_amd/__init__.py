@@ -20,12 +20,16 @@ from .binding import (  # noqa: F401
     absmax_quant_gemm_fp8_running,
     lib,
     merge_states,
+    row_inertia,
+    row_variance,
     rf_absmax_quant_fp8,
     rf_absmax_quant_gemm_fp8,
     rf_absmax_quant_gemm_fp8_running,
     rf_attn_decode_split,
     rf_attn_fwd,
     rf_merge_states,
+    rf_row_inertia,
+    rf_row_variance,
     rf_softmax,
     rf_softmax_topk,
     softmax,

@@ -30,6 +30,8 @@ SIGNATURES = {
     "rf_merge_states": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
     "rf_softmax_topk": [_P, _I, _I, _I, _I, _P, _P, _P],
     "rf_softmax": [_P, _I, _I, _I, _P, _P, _P],
+    "rf_row_variance": [_P, _I, _I, _I, _P, _P, _P],
+    "rf_row_inertia": [_P, _P, _I, _I, _I, _P, _P, _P],
     "rf_absmax_quant_fp8": [_P, _I, _I, _P, _P, _P],
     "rf_absmax_quant_gemm_fp8": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
     "rf_absmax_quant_gemm_fp8_running": [_P, _P, _P, _I, _I, _I, _P, _P, _P],
@@ -144,6 +146,23 @@ def rf_softmax(x, level, work, y):
     _check(lib().rf_softmax(_ptr(x), T, E, int(level), _ptr(work), _ptr(y), _stream(x)))
 
 
+def rf_row_variance(x, level, mean, var):
+    _dev(x, mean, var)
+    if x.dtype != torch.float32:
+        raise ValueError("rf_row_variance takes fp32 x")
+    T, E = x.shape
+    _check(lib().rf_row_variance(_ptr(x), T, E, int(level), _ptr(mean), _ptr(var), _stream(x)))
+
+
+def rf_row_inertia(x, w, level, centre, inertia):
+    _dev(x, w, centre, inertia)
+    if x.dtype != torch.float32 or w.dtype != torch.float32 or w.shape != x.shape:
+        raise ValueError("rf_row_inertia takes fp32 x and w of one shape")
+    T, E = x.shape
+    _check(lib().rf_row_inertia(_ptr(x), _ptr(w), T, E, int(level), _ptr(centre), _ptr(inertia),
+                                _stream(x)))
+
+
 def rf_absmax_quant_fp8(x, q, scale):
     _dev(x, q, scale)
     rows, cols = x.shape
@@ -213,6 +232,22 @@ def softmax(x, level=RF_FUSE_BLOCK):
     work = torch.empty(2 * x.shape[0], dtype=torch.float32, device=x.device) if level == RF_FUSE_NONE else None
     rf_softmax(x, level, work, y)
     return y
+
+
+def row_variance(x, level=RF_FUSE_WAVE):
+    """Per-row mean and population variance of fp32 x [T, E]."""
+    mean = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    var = torch.empty_like(mean)
+    rf_row_variance(x, level, mean, var)
+    return mean, var
+
+
+def row_inertia(x, w, level=RF_FUSE_WAVE):
+    """Per-row centre of mass and moment of inertia about it."""
+    centre = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    inertia = torch.empty_like(centre)
+    rf_row_inertia(x, w, level, centre, inertia)
+    return centre, inertia
 
 
 def absmax_quant_fp8(x):

@@ -149,6 +149,36 @@ rf_status rf_softmax(const float* x, int T, int E, int level, float* work, float
   return from_launch(rf::launch_softmax_rows(x, T, E, level, work, y, stream), "rf_softmax");
 }
 
+rf_status rf_row_variance(const float* x, int T, int E, int level, float* mean, float* var,
+                          hipStream_t stream) {
+  RF_REQUIRE(T >= 0 && E >= 0, RF_ERR_INVALID_ARG, "rf_row_variance: negative size");
+  RF_REQUIRE(level >= RF_FUSE_NONE && level <= RF_FUSE_BLOCK, RF_ERR_INVALID_ARG,
+             "rf_row_variance: unknown fusion level %d", level);
+  if (T == 0) return ok();
+  RF_REQUIRE(E >= 4 && E % 4 == 0, RF_ERR_INVALID_ARG, "rf_row_variance: E=%d must be a positive multiple of 4", E);
+  RF_REQUIRE(E <= 8192, RF_ERR_UNSUPPORTED, "rf_row_variance: E=%d > 8192", E);
+  RF_REQUIRE(x && mean && var, RF_ERR_INVALID_ARG, "rf_row_variance: null tensor pointer");
+  RF_REQUIRE(aligned(x, 16) && aligned(mean, 4) && aligned(var, 4), RF_ERR_INVALID_ARG,
+             "rf_row_variance: misaligned pointer");
+  RF_REQUIRE((long long)T * E < (1LL << 40), RF_ERR_INVALID_ARG, "rf_row_variance: problem too large");
+  return from_launch(rf::launch_row_variance(x, T, E, level, mean, var, stream), "rf_row_variance");
+}
+
+rf_status rf_row_inertia(const float* x, const float* w, int T, int E, int level, float* centre,
+                         float* inertia, hipStream_t stream) {
+  RF_REQUIRE(T >= 0 && E >= 0, RF_ERR_INVALID_ARG, "rf_row_inertia: negative size");
+  RF_REQUIRE(level >= RF_FUSE_NONE && level <= RF_FUSE_BLOCK, RF_ERR_INVALID_ARG,
+             "rf_row_inertia: unknown fusion level %d", level);
+  if (T == 0) return ok();
+  RF_REQUIRE(E >= 4 && E % 4 == 0, RF_ERR_INVALID_ARG, "rf_row_inertia: E=%d must be a positive multiple of 4", E);
+  RF_REQUIRE(E <= 8192, RF_ERR_UNSUPPORTED, "rf_row_inertia: E=%d > 8192", E);
+  RF_REQUIRE(x && w && centre && inertia, RF_ERR_INVALID_ARG, "rf_row_inertia: null tensor pointer");
+  RF_REQUIRE(aligned(x, 16) && aligned(w, 16) && aligned(centre, 4) && aligned(inertia, 4),
+             RF_ERR_INVALID_ARG, "rf_row_inertia: misaligned pointer");
+  RF_REQUIRE((long long)T * E < (1LL << 40), RF_ERR_INVALID_ARG, "rf_row_inertia: problem too large");
+  return from_launch(rf::launch_row_inertia(x, w, T, E, level, centre, inertia, stream), "rf_row_inertia");
+}
+
 rf_status rf_absmax_quant_fp8(const void* x, int rows, int cols, uint8_t* q, float* scale,
                               hipStream_t stream) {
   RF_REQUIRE(rows >= 0 && cols >= 0, RF_ERR_INVALID_ARG, "rf_absmax_quant_fp8: negative size");

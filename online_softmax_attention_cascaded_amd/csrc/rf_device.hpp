@@ -104,18 +104,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ---------------------------------------------------------------- wavefront reductions
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 // Sum and max over lanes l and l ^ 32 without LDS: v_permlane32_swap (gfx950)
 // applied to (x, x) returns x[l % 32] and x[32 + l % 32] in every lane l, so
 // both lanes of a pair combine the same two values in the same order.
@@ -126,6 +114,46 @@ __device__ __forceinline__ float half_swap_max(float x) {
 __device__ __forceinline__ float half_swap_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// The same across the two 16-lane rows of each half-wave (v_permlane16_swap):
+// lane l combines x[l & ~16] and x[l | 16].
+__device__ __forceinline__ float row_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Lane exchanges within a 16-lane row by DPP (no LDS): quad permutations
+// xor 1 and xor 2, then the half-row mirror (lane i <-> 7 - i in each 8) and
+// the row mirror (i <-> 15 - i). After the four steps of a commutative
+// operation every lane of the row holds the row's result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfRowMirror = 0x141, kDppRowMirror = 0x140;
+
+// Max and sum over the 64 lanes of a fully active wave: four DPP steps inside
+// each row, then the row and half-wave swaps. Every lane gets the same value
+// (each step combines the same two operands in the same order in both lanes
+// of a pair).
+__device__ __forceinline__ float wave_max(float v) {
+  v = __builtin_fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = __builtin_fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = __builtin_fmaxf(v, dpp_f32<kDppHalfRowMirror>(v));
+  v = __builtin_fmaxf(v, dpp_f32<kDppRowMirror>(v));
+  return half_swap_max(row_swap_max(v));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppHalfRowMirror>(v);
+  v += dpp_f32<kDppRowMirror>(v);
+  return half_swap_sum(row_swap_sum(v));
 }
 
 // Merge of two online-softmax statistics (m, l): both rescaled to the larger max.

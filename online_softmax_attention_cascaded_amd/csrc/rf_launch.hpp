@@ -30,6 +30,12 @@ hipError_t launch_softmax_topk(const float* logits, int T, int E, int k, int ren
 hipError_t launch_softmax_rows(const float* x, int T, int E, int level, float* work, float* y,
                                hipStream_t stream);
 
+hipError_t launch_row_variance(const float* x, int T, int E, int level, float* mean, float* var,
+                               hipStream_t stream);
+
+hipError_t launch_row_inertia(const float* x, const float* w, int T, int E, int level,
+                              float* centre, float* inertia, hipStream_t stream);
+
 hipError_t launch_absmax_quant_fp8(const void* x, int rows, int cols, uint8_t* q, float* scale,
                                    hipStream_t stream);
 

@@ -55,7 +55,7 @@ def test_argument_counts_match_header():
 
 
 def test_status_helpers(lib):
-    assert lib.rf_abi_version() == 3
+    assert lib.rf_abi_version() == 4
     assert lib.rf_status_string(OK) == b"RF_OK"
     assert lib.rf_status_string(INVALID) == b"RF_ERR_INVALID_ARG"
     assert lib.rf_status_string(UNSUPPORTED) == b"RF_ERR_UNSUPPORTED"
@@ -153,6 +153,30 @@ def test_softmax_validation(lib):
     assert f(FAKE, 10, 1024, 1, None, None, None) == INVALID
     assert f(None, 0, 1024, 0, None, None, None) == OK
     assert lib.rf_last_error() == b""
+
+
+@pytest.mark.parametrize("name", ["rf_row_variance", "rf_row_inertia"])
+def test_moments_validation(lib, name):
+    weighted = name == "rf_row_inertia"
+
+    def call(x=FAKE, w=FAKE, T=10, E=1024, level=2, c=FAKE, i=FAKE):
+        args = [x] + ([w] if weighted else []) + [T, E, level, c, i, None]
+        return getattr(lib, name)(*args)
+
+    assert call(level=4) == INVALID
+    assert call(level=-1) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(E=1022) == INVALID
+    assert call(E=0) == INVALID
+    assert call(E=8196) == UNSUPPORTED
+    assert call(x=None) == INVALID
+    assert call(i=None) == INVALID
+    assert call(x=MISALIGNED) == INVALID
+    if weighted:
+        assert call(w=None) == INVALID
+        assert call(w=MISALIGNED) == INVALID
+    assert lib.rf_last_error().startswith(name.encode())
+    assert call(x=None, w=None, T=0, c=None, i=None) == OK
 
 
 def test_quant_validation(lib):
