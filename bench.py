@@ -72,7 +72,8 @@ def gemm_flops():
 
 def read_traffic():
     """Measured HBM traffic per launch from profiles/traffic.txt, kept only while
-    the kernel source it was measured on is unchanged (matching hash)."""
+    the kernel source it was measured on, and the device header every kernel
+    includes, are unchanged (matching hash of the two files' bytes)."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "traffic.txt")
@@ -87,7 +88,8 @@ def read_traffic():
         src_path = os.path.join(ROOT, src)
         if not os.path.exists(src_path):
             continue
-        now = hashlib.sha256(open(src_path, "rb").read()).hexdigest()[:16]
+        header = os.path.join(ROOT, "online_softmax_attention_cascaded_amd", "csrc", "rf_device.hpp")
+        now = hashlib.sha256(open(src_path, "rb").read() + open(header, "rb").read()).hexdigest()[:16]
         if now == digest:
             out[kernel] = float(nbytes)
     return out
