@@ -19,10 +19,12 @@
 //  * K runs one tile ahead of V: while the softmax of tile t runs on the VALU,
 //    the scores of tile t+1 are already being computed on the matrix cores.
 //    Two LDS buffers per operand; one barrier per tile.
-//  * The reference max is moved only when a score exceeds it by more than 2^8
-//    (in exp2 units), which is rare after the first tile; l and the accumulator
-//    always share the same reference, so O = acc / l and lse = m + ln l are
-//    exact whatever the reference.
+//  * The reference max is moved only when a score exceeds it by more than 8 (in
+//    exp2 units: a probability above 2^8), which is rare after the first tile;
+//    l and the accumulator always share the same reference, so O = acc / l and
+//    lse = m + ln l are exact whatever the reference. The per-tile row max is
+//    only taken when a lane's probability sum shows that the bound may have
+//    been crossed.
 //  * Workgroups of one (batch, head) are placed on the same XCD (workgroups are
 //    dealt round-robin to the 8 XCDs), so its K/V stream is shared in one L2.
 //    Causal blocks are issued longest first.
@@ -37,6 +39,7 @@ constexpr int BM = 128;                 // query rows per workgroup, 32 per wave
 constexpr int BN = 64;                  // keys per tile
 constexpr int kTileBytes = BN * D * 2;  // 16 KB per operand tile
 constexpr float kTau = 8.f;             // lazy-rescale threshold, exp2 units
+constexpr float kPmax = 256.f;          // 2^kTau: largest probability against the reference
 constexpr int KA = 3;                   // K fragment reads run this many MFMAs ahead
 constexpr int VA = 4;                   // V^T fragment reads run this many MFMAs ahead
 
@@ -186,17 +189,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
         if (key1 >= Lk || (CAUSAL && key1 > qrow)) cur.s1[r] = kNegInf;
       }
     }
-    // Row max: four independent max3 chains, then the two halves of the wave.
-    float m4[4];
+    // Row max (four independent max3 chains, then the two halves of the wave),
+    // in exp2 units, and the move of the reference when some row's max exceeds
+    // it by more than kTau: l and the accumulator are rescaled with it.
+    auto row_max_c = [&]() {
+      float m4[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m4[j] = __builtin_fmaxf(cur.s0[j], cur.s1[j]);
+      for (int j = 0; j < 4; ++j) m4[j] = __builtin_fmaxf(cur.s0[j], cur.s1[j]);
 #pragma unroll
-    for (int r = 4; r < 16; ++r) m4[r & 3] = max3(m4[r & 3], cur.s0[r], cur.s1[r]);
-    const float mx = half_swap_max(__builtin_fmaxf(__builtin_fmaxf(m4[0], m4[1]), __builtin_fmaxf(m4[2], m4[3])));
-    const float mxc = mx * c;
-    if (t == 0) {
-      m_c = mxc;  // every row sees key 0, so this is finite
-    } else if (__any(mxc > m_c + kTau)) {
+      for (int r = 4; r < 16; ++r) m4[r & 3] = max3(m4[r & 3], cur.s0[r], cur.s1[r]);
+      return half_swap_max(__builtin_fmaxf(__builtin_fmaxf(m4[0], m4[1]), __builtin_fmaxf(m4[2], m4[3]))) * c;
+    };
+    auto move_reference = [&](float mxc) {
+      if (!__any(mxc > m_c + kTau)) return false;
       float alpha = 1.f;
       if (mxc > m_c + kTau) {
         alpha = fast_exp2(m_c - mxc);
@@ -205,7 +210,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-    }
+      return true;
+    };
+    // Tile 0 sets the reference (every row sees key 0, so it is finite). Later
+    // tiles compute their probabilities against the current reference first,
+    // without a max: a lane's probabilities are each at most their sum, so
+    // while no lane's sum exceeds 2^kTau no score rose above the reference by
+    // more than kTau and nothing has to move. Otherwise the max is taken, the
+    // reference moved if needed and the probabilities recomputed (rare after
+    // the first tiles).
+    if (t == 0) m_c = row_max_c();
     // ---- one basic block: the 16 score MFMAs of tile t+1, each K fragment read
     // KA MFMAs ahead (the fences keep every read next to its MFMA), and the
     // probabilities of tile t (2 fma, 2 exp2, 1 bf16 pack, 2 adds per pair). The
@@ -239,6 +253,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       rs += p0 + p1;
       pw[ks][jj] = pack_bf16x2(p0, p1);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (t > 0 && __any(rs > kPmax) && move_reference(row_max_c())) {
+      rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ks = i >> 2, jj = i & 3;
+        const f32x16& src = (ks < 2) ? cur.s0 : cur.s1;
+        const int e = 8 * (ks & 1) + 2 * jj;
+        const float p0 = fast_exp2(fmaf(src[e], c, -m_c));
+        const float p1 = fast_exp2(fmaf(src[e + 1], c, -m_c));
+        rs += p0 + p1;
+        pw[ks][jj] = pack_bf16x2(p0, p1);
+      }
     }
     l_run += half_swap_sum(rs);
     // O^T += V^T P^T; consecutive MFMAs update different accumulators. MFMA i

@@ -80,6 +80,32 @@ def test_bf16_large_scores():
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_bf16_reference_moves(causal):
+    """Scores set tile by tile (scale ln 2, so scores are in exp2 units): tile 0
+    at 0, tile 1 at 7 (every probability 2^7: each lane's sum passes 2^8 but no
+    score passes the reference by more than 8, so nothing may move), tile 2 at
+    20 and tile 3 at 27.5 (the reference must move and the tile be recomputed),
+    then back down, with a ragged last tile. Rows scale the scores by 1 + r/64."""
+    print_case(test="bf16_reference_moves", causal=causal)
+    d, Lk = 128, 6 * 64 + 17
+    Lq = Lk if causal else 70
+    levels = [0.0, 7.0, 20.0, 27.5, 10.0, 26.0, 3.0]
+    kk = np.zeros((1, 1, Lk, d), np.float32)
+    for j in range(Lk):
+        kk[0, 0, j, 0] = levels[j // 64]
+    kk[0, 0, :, 1] = np.random.default_rng(5).standard_normal(Lk) * 0.25
+    qq = np.zeros((1, 1, Lq, d), np.float32)
+    qq[0, 0, :, 0] = 1.0 + np.arange(Lq) / 64.0
+    qq[0, 0, :, 1] = 1.0
+    vv = np.random.default_rng(6).standard_normal((1, 1, Lk, d)).astype(np.float32)
+    q, k, v = inputs.as_bf16(qq), inputs.as_bf16(kk), inputs.as_bf16(vv)
+    scale = math.log(2.0)
+    o, lse = rf.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal=causal)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal)
+    assert_bf16_attention(np32(o), o_ref, np32(lse), lse_ref, what=f"reference moves causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_bf16_prefill_config_sampled(causal):
     """The prefill workload at full size, B=4, H=32, L=2048, d=128, in the launch
     configuration the bench times; the oracle checks 4 sampled (batch, head) pairs."""
