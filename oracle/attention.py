@@ -63,18 +63,21 @@ def _f64(x):
 def attention(q, k, v, scale, causal=False):
     """Unfused safe-softmax attention.
 
-    q: [B, Hq, Lq, d]; k, v: [B, Hkv, Lk, d] (any float dtype, upcast exactly).
-    Returns (o [B, Hq, Lq, d] float64, lse [B, Hq, Lq] float64).
+    q: [B, Hq, Lq, d]; k: [B, Hkv, Lk, d]; v: [B, Hkv, Lk, dv] (any float
+    dtype, upcast exactly; dv may differ from d, as in multi-latent attention
+    where the values are the first dv columns of the shared latent rows).
+    Returns (o [B, Hq, Lq, dv] float64, lse [B, Hq, Lq] float64).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Hq, Lq, d = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
+    dv = v.shape[-1]
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     if causal and Lq != Lk:
         raise ValueError("causal attention is defined here for Lq == Lk only")
     group = Hq // Hkv
-    o = np.zeros((B, Hq, Lq, d))
+    o = np.zeros((B, Hq, Lq, dv))
     lse = np.zeros((B, Hq, Lq))
     if causal:
         visible = np.tril(np.ones((Lq, Lk), dtype=bool))
@@ -107,8 +110,9 @@ def attention_online(q, k, v, scale, causal=False, tile=64):
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Hq, Lq, d = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
+    dv = v.shape[-1]
     group = Hq // Hkv
-    o = np.zeros((B, Hq, Lq, d))
+    o = np.zeros((B, Hq, Lq, dv))
     lse = np.zeros((B, Hq, Lq))
     trace = []
     for b in range(B):
@@ -117,7 +121,7 @@ def attention_online(q, k, v, scale, causal=False, tile=64):
             for i in range(Lq):
                 m = NEG_INF
                 l = 0.0
-                acc = np.zeros(d)
+                acc = np.zeros(dv)
                 for t0 in range(0, Lk, tile):
                     t1 = min(t0 + tile, Lk)
                     scores = scale * (k[b, hk, t0:t1] @ q[b, h, i])
@@ -150,14 +154,15 @@ def segment_bounds(Lk, S):
 def decode_partials(q, k, v, scale, S, bounds=None):
     """Per-segment partial states for single-query decode.
 
-    q: [B, Hq, d]; k, v: [B, Hkv, Lk, d]. ``bounds`` optionally replaces the
-    ceil-div segmentation by an explicit list of S (start, end) key ranges.
-    Returns m [B, Hq, S], l [B, Hq, S], acc [B, Hq, S, d] (float64),
-    acc unnormalised and relative to m.
+    q: [B, Hq, d]; k: [B, Hkv, Lk, d]; v: [B, Hkv, Lk, dv]. ``bounds``
+    optionally replaces the ceil-div segmentation by an explicit list of S
+    (start, end) key ranges. Returns m [B, Hq, S], l [B, Hq, S],
+    acc [B, Hq, S, dv] (float64), acc unnormalised and relative to m.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Hq, d = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
+    dv = v.shape[-1]
     group = Hq // Hkv
     if bounds is None:
         bounds = segment_bounds(Lk, S)
@@ -165,7 +170,7 @@ def decode_partials(q, k, v, scale, S, bounds=None):
         raise ValueError("need one key range per segment")
     m = np.full((B, Hq, S), NEG_INF)
     l = np.zeros((B, Hq, S))
-    acc = np.zeros((B, Hq, S, d))
+    acc = np.zeros((B, Hq, S, dv))
     for b in range(B):
         for h in range(Hq):
             hk = h // group

@@ -176,6 +176,32 @@ def test_matches_torch_sdpa_float64(causal):
     assert np.allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-13)
 
 
+def test_latent_values_narrower_than_keys():
+    """Multi-latent form: one shared latent row per key serves as the key (all
+    dk columns) and as the value (its first dv columns). Pinned by torch's
+    float64 attention with a narrower value width, and by linearity in V: the
+    output equals the first dv columns of the output with v = k."""
+    B, H, L, dk, dv = 2, 8, 37, 24, 16
+    q = _rand(31, B, H, 1, dk)
+    lat = _rand(32, B, 1, L, dk)
+    scale = 1 / math.sqrt(dk)
+    o, lse = oracle.attention(q, lat, lat[..., :dv], scale)
+    tq, tk = torch.from_numpy(q), torch.from_numpy(lat).expand(B, H, L, dk)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tk[..., :dv], scale=scale)
+    assert o.shape == (B, H, 1, dv)
+    assert np.allclose(o, ref.numpy(), rtol=0, atol=1e-13)
+    o_full, lse_full = oracle.attention(q, lat, lat, scale)
+    assert np.allclose(o, o_full[..., :dv], rtol=0, atol=1e-15)
+    assert np.array_equal(lse, lse_full)
+    # decode partials with the narrower values merge to the same result
+    m, l, acc = oracle.decode_partials(q[:, :, 0], lat, lat[..., :dv], scale, 3)
+    assert acc.shape == (B, H, 3, dv)
+    om, lm = oracle.merge_states(m, l, acc)
+    assert np.allclose(om, o[:, :, 0], rtol=0, atol=1e-14) and np.allclose(lm, lse[:, :, 0], rtol=0, atol=1e-14)
+    oo, lo, _ = oracle.attention_online(q, lat, lat[..., :dv], scale, tile=5)
+    assert np.allclose(oo, o, rtol=0, atol=1e-14)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("tile", [1, 3, 16, 64])
 def test_online_equals_unfused(causal, tile):
