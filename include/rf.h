@@ -13,6 +13,8 @@
  *     (transcript cues 21 and 39; "RedFuser episode visual explainer",
  *     widgets "Merging partial states across blocks (FlashDecoding-style)"
  *     and "Single-Segment vs Multi-Segment");
+ *   - the same split over a shared latent cache (multi-latent attention,
+ *     transcript cues 41 and 55);
  *   - MoE routing: softmax followed by top-k (transcript cue 11;
  *     "Online normalizer calculation for softmax", abstract);
  *   - safe softmax alone, fused at the thread, wave or workgroup level of the
@@ -46,7 +48,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 4
+#define RF_ABI_VERSION 5
 
 typedef enum {
   RF_OK = 0,
@@ -107,6 +109,27 @@ rf_status rf_attn_decode_split(rf_dtype dt, const void* q, const void* k, const 
 rf_status rf_merge_states(const float* part_m, const float* part_l, const float* part_acc,
                           int rows, int S, int d, rf_dtype out_dt, void* o, float* lse,
                           hipStream_t stream);
+
+/*
+ * rf_mla_decode_split -- split-KV decode over a shared latent cache
+ * (multi-latent attention: transcript cues 41 and 55 name the multi-latent
+ * decode workload; the split and the partial states are those of
+ * rf_attn_decode_split, cues 21 and 39). Every key is one latent row; the
+ * score of query head h is scale * q_h . row over all Dqk columns, its value
+ * is the row's first Dv columns, and all H heads of a sequence share the rows.
+ * Writes the same unnormalised partial states as rf_attn_decode_split, to be
+ * merged by rf_merge_states with d = Dv.
+ *
+ *   q        [B, H, Dqk] bf16
+ *   kv       [B, Lk, Dqk] bf16 (latent rows)
+ *   part_m, part_l [B, H, S] fp32;  part_acc [B, H, S, Dv] fp32 (16-byte aligned)
+ *   Dqk == 576 and Dv == 512 (else RF_ERR_UNSUPPORTED); H a multiple of 16, at
+ *   most 128 (each group of 16 heads streams the cache once); segments of
+ *   ceil(Lk / S) keys, empty ones written as the identity (-inf, 0, 0).
+ */
+rf_status rf_mla_decode_split(const void* q, const void* kv, float* part_m, float* part_l,
+                              float* part_acc, int B, int H, int Lk, int Dqk, int Dv, int S,
+                              float scale, hipStream_t stream);
 
 /*
  * rf_softmax_topk -- MoE routing: per row of logits, softmax then top-k

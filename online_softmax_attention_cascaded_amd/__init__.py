@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     absmax_quant_gemm_fp8_running,
     lib,
     merge_states,
+    mla_decode,
     row_inertia,
     row_variance,
     rf_absmax_quant_fp8,
@@ -28,6 +29,7 @@ from .binding import (  # noqa: F401
     rf_attn_decode_split,
     rf_attn_fwd,
     rf_merge_states,
+    rf_mla_decode_split,
     rf_row_inertia,
     rf_row_variance,
     rf_softmax,

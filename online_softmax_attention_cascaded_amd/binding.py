@@ -28,6 +28,7 @@ SIGNATURES = {
     "rf_attn_fwd": [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P],
     "rf_attn_decode_split": [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
     "rf_merge_states": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
+    "rf_mla_decode_split": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
     "rf_softmax_topk": [_P, _I, _I, _I, _I, _P, _P, _P],
     "rf_softmax": [_P, _I, _I, _I, _P, _P, _P],
     "rf_row_variance": [_P, _I, _I, _I, _P, _P, _P],
@@ -123,6 +124,17 @@ def rf_attn_decode_split(q, k, v, part_m, part_l, part_acc, scale):
                                       float(scale), _stream(q)))
 
 
+def rf_mla_decode_split(q, kv, part_m, part_l, part_acc, scale):
+    _dev(q, kv, part_m, part_l, part_acc)
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
+        raise ValueError("rf_mla_decode_split takes bf16 q and latent rows")
+    B, H, Dqk = q.shape
+    Lk = kv.shape[1]
+    S, Dv = part_acc.shape[2], part_acc.shape[3]
+    _check(lib().rf_mla_decode_split(_ptr(q), _ptr(kv), _ptr(part_m), _ptr(part_l), _ptr(part_acc),
+                                     B, H, Lk, Dqk, Dv, S, float(scale), _stream(q)))
+
+
 def rf_merge_states(part_m, part_l, part_acc, o, lse):
     _dev(part_m, part_l, part_acc, o, lse)
     S, d = part_acc.shape[-2], part_acc.shape[-1]
@@ -216,6 +228,17 @@ def attn_decode(q, k, v, scale, S, out_dtype=torch.bfloat16):
     parts = attn_decode_partials(q, k, v, scale, S)
     o, lse = merge_states(*parts, out_dtype=out_dtype)
     return o, lse, parts
+
+
+def mla_decode(q, kv, scale, S, dv=512, out_dtype=torch.bfloat16):
+    """Split-KV decode over a shared latent cache, then the merge of the partials."""
+    B, H, _ = q.shape
+    part_m = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    part_l = torch.empty_like(part_m)
+    part_acc = torch.empty((B, H, S, dv), dtype=torch.float32, device=q.device)
+    rf_mla_decode_split(q, kv, part_m, part_l, part_acc, scale)
+    o, lse = merge_states(part_m, part_l, part_acc, out_dtype=out_dtype)
+    return o, lse, (part_m, part_l, part_acc)
 
 
 def softmax_topk(logits, k, renormalize=True):

@@ -98,6 +98,34 @@ rf_status rf_attn_decode_split(rf_dtype dt, const void* q, const void* k, const 
                      "rf_attn_decode_split");
 }
 
+rf_status rf_mla_decode_split(const void* q, const void* kv, float* part_m, float* part_l,
+                              float* part_acc, int B, int H, int Lk, int Dqk, int Dv, int S,
+                              float scale, hipStream_t stream) {
+  RF_REQUIRE(B >= 0 && H >= 0 && Lk >= 0 && Dqk >= 0 && Dv >= 0, RF_ERR_INVALID_ARG,
+             "rf_mla_decode_split: negative size");
+  RF_REQUIRE(S >= 1, RF_ERR_INVALID_ARG, "rf_mla_decode_split: S=%d must be >= 1", S);
+  if ((long long)B * H == 0) return ok();
+  RF_REQUIRE(Lk >= 1, RF_ERR_INVALID_ARG, "rf_mla_decode_split: Lk must be >= 1");
+  RF_REQUIRE(Dv >= 1 && Dv <= Dqk, RF_ERR_INVALID_ARG,
+             "rf_mla_decode_split: value width %d must be in 1..%d", Dv, Dqk);
+  RF_REQUIRE(q && kv && part_m && part_l && part_acc, RF_ERR_INVALID_ARG,
+             "rf_mla_decode_split: null tensor pointer");
+  RF_REQUIRE(aligned(q, 16) && aligned(kv, 16) && aligned(part_acc, 16) && aligned(part_m, 4) &&
+                 aligned(part_l, 4),
+             RF_ERR_INVALID_ARG, "rf_mla_decode_split: misaligned pointer");
+  RF_REQUIRE(scale == scale, RF_ERR_INVALID_ARG, "rf_mla_decode_split: scale is NaN");
+  RF_REQUIRE(Dqk == 576 && Dv == 512, RF_ERR_UNSUPPORTED,
+             "rf_mla_decode_split: widths %d/%d (need 576 for keys, 512 for values)", Dqk, Dv);
+  RF_REQUIRE(H % 16 == 0 && H <= 128, RF_ERR_UNSUPPORTED,
+             "rf_mla_decode_split: H=%d (need a multiple of 16, at most 128)", H);
+  RF_REQUIRE((long long)(Lk + 96) * Dqk * 2 < (1LL << 31), RF_ERR_UNSUPPORTED,
+             "rf_mla_decode_split: one sequence's cache reaches 2 GiB");
+  RF_REQUIRE((long long)B * S * (H / 16) < (1LL << 31) && (long long)B * H * S * Dv < (1LL << 40),
+             RF_ERR_INVALID_ARG, "rf_mla_decode_split: problem too large");
+  return from_launch(rf::launch_mla_decode_split(q, kv, part_m, part_l, part_acc, B, H, Lk, S, scale, stream),
+                     "rf_mla_decode_split");
+}
+
 rf_status rf_merge_states(const float* part_m, const float* part_l, const float* part_acc,
                           int rows, int S, int d, rf_dtype out_dt, void* o, float* lse,
                           hipStream_t stream) {

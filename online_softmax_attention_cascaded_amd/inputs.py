@@ -13,6 +13,9 @@ pages do not print):
 * tiny fp32 attention: B=1, H=1, Lq=64, Lk=256, d=64;
 * prefill: B=4, H=32, Lq=Lk=2048, d=128, bf16;
 * decode: B=8, Hq=32, Hkv=8, Lk=32768, d=128, bf16 KV cache;
+* multi-latent decode: B=32 sequences, 16 query heads (one tensor-parallel
+  shard), Lk=8192 latent rows of 576 bf16 values (512 latent + 64 positional),
+  values = the first 512 columns;
 * routing: 16384 tokens x 256 experts fp32 logits, 1 % of rows with +6 on one
   random expert;
 * safe softmax: rows of 1024 .. 8192 fp32 values, 2^26 values in all;
@@ -53,6 +56,14 @@ def decode_inputs(seed, B, Hq, Hkv, Lk, d):
     k = as_bf16(normal(rng, (B, Hkv, Lk, d)))
     v = as_bf16(normal(rng, (B, Hkv, Lk, d)))
     return q, k, v
+
+
+def mla_inputs(seed, B, H, Lk, dqk=576):
+    """q [B,H,dqk] and latent rows [B,Lk,dqk] ~ N(0,1), bf16 torch CPU tensors."""
+    rng = np.random.default_rng(seed)
+    q = as_bf16(normal(rng, (B, H, dqk)))
+    kv = as_bf16(normal(rng, (B, Lk, dqk)))
+    return q, kv
 
 
 def worked_example_decode(d=128):

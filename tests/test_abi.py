@@ -55,7 +55,7 @@ def test_argument_counts_match_header():
 
 
 def test_status_helpers(lib):
-    assert lib.rf_abi_version() == 4
+    assert lib.rf_abi_version() == 5
     assert lib.rf_status_string(OK) == b"RF_OK"
     assert lib.rf_status_string(INVALID) == b"RF_ERR_INVALID_ARG"
     assert lib.rf_status_string(UNSUPPORTED) == b"RF_ERR_UNSUPPORTED"
@@ -117,6 +117,37 @@ def decode(lib, dt=BF16, q=FAKE, k=FAKE, v=FAKE, m=FAKE, l=FAKE, acc=FAKE, B=1, 
 )
 def test_decode_validation(lib, kw, expect):
     assert decode(lib, **kw) == expect
+
+
+def mla(lib, q=FAKE, kv=FAKE, m=FAKE, l=FAKE, acc=FAKE, B=2, H=16, Lk=100, Dqk=576, Dv=512, S=4,
+        scale=0.1):
+    return lib.rf_mla_decode_split(q, kv, m, l, acc, B, H, Lk, Dqk, Dv, S, scale, None)
+
+
+@pytest.mark.parametrize(
+    "kw,expect",
+    [
+        (dict(S=0), INVALID),
+        (dict(Lk=0), INVALID),
+        (dict(B=-1), INVALID),
+        (dict(Dv=600), INVALID),
+        (dict(acc=None), INVALID),
+        (dict(kv=MISALIGNED), INVALID),
+        (dict(scale=float("nan")), INVALID),
+        (dict(Dqk=192, Dv=128), UNSUPPORTED),
+        (dict(Dv=256), UNSUPPORTED),
+        (dict(H=8), UNSUPPORTED),
+        (dict(H=144), UNSUPPORTED),
+        (dict(Lk=1 << 21), UNSUPPORTED),   # one sequence's cache reaches 2 GiB
+    ],
+)
+def test_mla_validation(lib, kw, expect):
+    assert mla(lib, **kw) == expect
+    assert lib.rf_last_error().startswith(b"rf_mla_decode_split")
+
+
+def test_mla_empty_is_ok_without_pointers(lib):
+    assert mla(lib, q=None, kv=None, m=None, l=None, acc=None, B=0) == OK
 
 
 def test_merge_validation(lib):

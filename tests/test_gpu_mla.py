@@ -1,0 +1,93 @@
+"""GPU parity of split-KV decode over a shared latent cache
+(rf_mla_decode_split + rf_merge_states, through the C ABI) against the fp64
+oracle: the partial states against oracle.decode_partials with the values
+taken as the first 512 columns of the latent rows, the merged output against
+oracle.attention. Bars as for split-KV decode: P enters the value product as
+a bf16 hi + lo pair (about 16-bit weights), everything else is fp32."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import online_softmax_attention_cascaded_amd as rf
+from online_softmax_attention_cascaded_amd import inputs
+from gpu_util import DEV, needs_gpu, normwise, np32, print_case
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+DQK, DV = 576, 512
+
+
+def _check(B, H, Lk, S, scale, seed=5, partials=True):
+    q, kv = inputs.mla_inputs(seed, B, H, Lk)
+    o, lse, (m, l, acc) = rf.mla_decode(q.to(DEV), kv.to(DEV), scale, S, out_dtype=torch.float32)
+    lat = kv[:, None]                      # [B, 1, Lk, 576]: one shared latent head
+    if partials:
+        m_ref, l_ref, acc_ref = oracle.decode_partials(q, lat, lat[..., :DV], scale, S)
+        m, l, acc = np32(m), np32(l), np32(acc)
+        empty = np.isinf(m_ref)
+        assert np.array_equal(np.isinf(m), empty)
+        assert np.all(l[empty] == 0) and np.all(acc[empty] == 0)
+        fin = ~empty
+        assert np.abs(m[fin] - m_ref[fin]).max() <= 1e-5 * max(1, np.abs(m_ref[fin]).max())
+        assert normwise(l[fin], l_ref[fin]) <= 1e-5
+        assert normwise(acc[fin], acc_ref[fin]) <= 1e-4
+    o_ref, lse_ref = oracle.attention(q[:, :, None], lat, lat[..., :DV], scale)
+    assert normwise(np32(o), o_ref[:, :, 0]) <= 1e-4
+    assert np.abs(np32(lse) - lse_ref[:, :, 0]).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+
+
+@pytest.mark.parametrize(
+    "B,H,Lk,S",
+    [
+        (1, 16, 1000, 1),
+        (1, 16, 1000, 4),
+        (2, 16, 777, 16),     # ragged last segment and ragged steps
+        (1, 16, 5, 4),        # segment lengths 2, 2, 1, 0: an empty segment
+        (1, 16, 100, 64),     # segment length 2: many trailing empty segments
+        (2, 32, 513, 3),      # two groups of 16 heads
+        (1, 128, 300, 2),     # eight head groups
+        (1, 16, 31, 1),       # fewer keys than a step
+        (1, 16, 32, 1),
+        (1, 16, 33, 2),
+    ],
+)
+def test_mla_partials_and_merge_small(B, H, Lk, S):
+    print_case(test="mla_small", B=B, H=H, Lk=Lk, S=S)
+    _check(B, H, Lk, S, 1 / math.sqrt(DQK))
+
+
+def test_mla_large_scores():
+    """scale 1 with N(0,1) rows: scores with a spread of about 24, so the
+    reference max moves often within a segment."""
+    print_case(test="mla_large_scores")
+    _check(2, 16, 2000, 3, 1.0)
+
+
+@pytest.mark.parametrize("S", [8, 16, 32])
+def test_mla_config_sampled(S):
+    """The measured workload, B=32 sequences, H=16, Lk=8192 latent rows of 576,
+    in the launch configuration the bench times; three sequences checked
+    against the oracle, every output finite."""
+    print_case(test="mla_config", S=S)
+    B, H, Lk = 32, 16, 8192
+    scale = 1 / math.sqrt(DQK)
+    q, kv = inputs.mla_inputs(9, B, H, Lk)
+    o, lse, _ = rf.mla_decode(q.to(DEV), kv.to(DEV), scale, S, out_dtype=torch.float32)
+    o, lse = np32(o), np32(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    for b in (0, 13, 31):
+        lat = kv[b:b + 1, None]
+        o_ref, lse_ref = oracle.attention(q[b:b + 1, :, None], lat, lat[..., :DV], scale)
+        assert normwise(o[b], o_ref[0, :, 0]) <= 1e-4
+        assert np.abs(lse[b] - lse_ref[0, :, 0]).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+
+
+def test_mla_deterministic():
+    q, kv = (t.to(DEV) for t in inputs.mla_inputs(3, 2, 32, 1500))
+    a = rf.mla_decode(q, kv, 0.05, 5)
+    b = rf.mla_decode(q, kv, 0.05, 5)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
