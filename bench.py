@@ -7,8 +7,9 @@ seeded input already resident in HBM:
     partial states + merge;
   MoE routing, 16384 x 256 fp32 logits, softmax -> top-8 (renormalised);
   FP8 per-token quantise + GEMM, M=N=4096, K=7168.
-After the timed steps, two alternatives are timed on their own: the one-pass
-running-scale FP8 GEMM, and safe softmax, variance and moment of inertia over
+After the timed steps, further rows are timed on their own: the one-pass
+running-scale FP8 GEMM, split-KV decode over a shared latent cache (B=32
+sequences, 16 heads, 8192 latent rows of 576 bf16 values), and safe softmax, variance and moment of inertia over
 rows of 1K..8K fp32 values at each fusion level of the reduction tree
 (unfused, thread, wave, block).
 Routing logits rotate over 20 buffers and the FP8 A operand over 5, so those
@@ -38,6 +39,8 @@ PREFILL = dict(B=4, H=32, L=2048, d=128)
 DECODE = dict(B=8, Hq=32, Hkv=8, Lk=32768, d=128)
 ROUTING = dict(T=16384, E=256, k=8)
 FP8 = dict(M=4096, N=4096, K=7168)
+MLA = dict(B=32, H=16, Lk=8192, dqk=576, dv=512)
+MLA_SEGMENTS = (8, 16, 32)
 SOFTMAX_VALUES = 1 << 26
 SOFTMAX_E = (1024, 2048, 4096, 8192)
 DECODE_SEGMENTS = (4, 16, 64)
@@ -342,6 +345,41 @@ def main():
         "bound": "mfma", "achieved": round(gemm_flops() / t_run / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
         "unit": "TFLOP/s", "frac": round(gemm_flops() / t_run / 1e12 / PEAK_FP8_TFLOPS, 4),
         "note": "single kernel: running per-row scale, A quantised inside the K loop"}
+    # Split-KV decode over a shared latent cache (multi-latent attention),
+    # partial states + merge, at each segment count. Algorithmic bytes: the
+    # latent rows once (B * Lk * 576 * 2) plus q and O.
+    Mq, Mkv = (t.to(dev) for t in inputs.mla_inputs(7, MLA["B"], MLA["H"], MLA["Lk"]))
+    mla_bytes = (MLA["B"] * MLA["Lk"] * MLA["dqk"] * 2 + MLA["B"] * MLA["H"] * MLA["dqk"] * 2
+                 + MLA["B"] * MLA["H"] * MLA["dv"] * 2)
+    mo = torch.empty((MLA["B"], MLA["H"], MLA["dv"]), dtype=torch.bfloat16, device=dev)
+    mlse = torch.empty((MLA["B"], MLA["H"]), device=dev)
+    mla_t = {}
+    for S in MLA_SEGMENTS:
+        pm = torch.empty((MLA["B"], MLA["H"], S), device=dev)
+        pl = torch.empty_like(pm)
+        pa = torch.empty((MLA["B"], MLA["H"], S, MLA["dv"]), device=dev)
+
+        def mla_call():
+            rf.rf_mla_decode_split(Mq, Mkv, pm, pl, pa, 1 / math.sqrt(MLA["dqk"]))
+            rf.rf_merge_states(pm, pl, pa, mo, mlse)
+        for _ in range(10):
+            mla_call()
+        e0.record()
+        for _ in range(args.steps):
+            mla_call()
+        e1.record()
+        torch.cuda.synchronize()
+        mla_t[S] = e0.elapsed_time(e1) / 1e3 / args.steps
+    best_mla = min(mla_t, key=mla_t.get)
+    result["us_per_launch"].update({f"mla_decode_s{S}": round(t * 1e6, 2) for S, t in mla_t.items()})
+    result["rooflines"]["mla_decode"] = {
+        "bound": "hbm", "segments": best_mla, "achieved": round(mla_bytes / mla_t[best_mla] / 1e9, 1),
+        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(mla_bytes / mla_t[best_mla] / 1e9 / PEAK_HBM_GBS, 4),
+        "by_segments": {str(S): round(mla_bytes / t / 1e9, 1) for S, t in mla_t.items()},
+        "note": "latent rows read once; split + merge timed together"}
+    del Mq, Mkv
+    progress("multi-latent decode timed")
+
     # Safe softmax alone at each fusion level of the reduction tree, rows of
     # 1K .. 8K fp32 values, 2^26 values per launch. The rate is counted with the
     # fused form's algorithmic bytes (x read once, y written once: 8 B/value)

@@ -335,7 +335,8 @@ __device__ __forceinline__ void fold_state(float& m, float& l, f32x4& acc, float
 // 128-column block and folds the states s = h, h + 2, ... with the rescale-
 // and-add rule (cue 21), loading kChunk states at a time so their loads are
 // in flight together; the two half-waves then merge their states and lanes of
-// the first half write the row. Blocks of 128 columns repeat for d > 128.
+// the first half write the row. Each 128-column block of a row is its own
+// wave (grid y), so wide rows do not serialise their blocks.
 constexpr int kChunk = 8;
 
 __global__ __launch_bounds__(64) void merge_states_kernel(const float* __restrict__ part_m,
@@ -349,7 +350,8 @@ __global__ __launch_bounds__(64) void merge_states_kernel(const float* __restric
   const float* mrow = part_m + row * S;
   const float* lrow = part_l + row * S;
   const float* arow = part_acc + row * S * d;
-  for (int c0 = 0; c0 < d; c0 += 128) {
+  {
+    const int c0 = 128 * blockIdx.y;
     const int col = c0 + 4 * c;
     const bool act = col < d;
     float m = kNegInf, l = 0.f;
@@ -407,8 +409,8 @@ hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
 hipError_t launch_merge_states(const float* part_m, const float* part_l, const float* part_acc,
                                int rows, int S, int d, int out_bf16, void* o, float* lse,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(merge_states_kernel, dim3(rows), dim3(64), 0, stream, part_m, part_l,
-                     part_acc, S, d, out_bf16, o, lse);
+  hipLaunchKernelGGL(merge_states_kernel, dim3(rows, (d + 127) / 128), dim3(64), 0, stream, part_m,
+                     part_l, part_acc, S, d, out_bf16, o, lse);
   return hipGetLastError();
 }
 

@@ -162,21 +162,27 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_kernel(
   issue(1);
   issue(2);
   for (int t = 0; t < nsteps; ++t) {
-    // loads of steps t+1 and t+2 may stay in flight
-    if (wave < 4)
-      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    // Every wave is done with step t-1: its stage takes step t+3 at once,
+    // before anyone waits for step t, so three steps stay in flight.
     lds_barrier();
     issue(t + 3);
+    // loads of steps t+1 .. t+3 may stay in flight
+    if (wave < 4)
+      asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    lds_barrier();
     const char* st = smem + (t % NST) * kStageBytes;
 
     // partial scores of keys 16 kt .. +15
-    f32x4 sp = {0.f, 0.f, 0.f, 0.f};
+    // two independent accumulation chains (even and odd k-steps)
+    f32x4 sp0 = {0.f, 0.f, 0.f, 0.f}, sp1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 6; ++j)
-      if (j < nks) sp = mfma16(*reinterpret_cast<const bf16x8_t*>(st + sofs[j]), qf[j], sp);
-    *reinterpret_cast<f32x4*>(spart + (wave * 64 + lane) * 4) = sp;
+    for (int j = 0; j < 6; j += 2) {
+      if (j < nks) sp0 = mfma16(*reinterpret_cast<const bf16x8_t*>(st + sofs[j]), qf[j], sp0);
+      if (j < nks) sp1 = mfma16(*reinterpret_cast<const bf16x8_t*>(st + sofs[j + 1]), qf[j + 1], sp1);
+    }
+    *reinterpret_cast<f32x4*>(spart + (wave * 64 + lane) * 4) = sp0 + sp1;
     lds_barrier();
     // full scores: lane holds keys 4 g4 + i (tile 0) and 16 + 4 g4 + i (tile 1)
     f32x4 sc[2];
@@ -234,17 +240,22 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_kernel(
       plo[j] = pack_bf16x2(a0 - bf16_lo(hi), a1 - bf16_hi(hi));
     }
     // O^T[c][head] += V^T[c][key] P^T[key][head]
+    // all eight transposing reads first, then each tile waits for its own two
     const uint32_t sa = lds_addr(st);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    u32x4 va[4];
+    static_for<4>([&](auto mc) {
+      constexpr int mt = decltype(mc)::value;
       const u32x2 r0 = lds_read_tr16<0>(sa + vofs[mt][0]);
       const u32x2 r1 = lds_read_tr16<0>(sa + vofs[mt][1]);
-      u32x4 va = {r0[0], r0[1], r1[0], r1[1]};
-      lds_wait_for<0>(va);
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, va);
+      va[mt] = u32x4{r0[0], r0[1], r1[0], r1[1]};
+    });
+    static_for<4>([&](auto mc) {
+      constexpr int mt = decltype(mc)::value;
+      lds_wait_for<2 * (3 - mt)>(va[mt]);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, va[mt]);
       oacc[mt] = mfma16(a, __builtin_bit_cast(bf16x8_t, phi), oacc[mt]);
       oacc[mt] = mfma16(a, __builtin_bit_cast(bf16x8_t, plo), oacc[mt]);
-    }
+    });
   }
   // drain the loads issued for steps past the end before the workgroup exits
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
