@@ -43,7 +43,7 @@ MLA = dict(B=32, H=16, Lk=8192, dqk=576, dv=512)
 MLA_SEGMENTS = (8, 16, 32)
 SOFTMAX_VALUES = 1 << 26
 SOFTMAX_E = (1024, 2048, 4096, 8192)
-DECODE_SEGMENTS = (4, 16, 64)
+DECODE_SEGMENTS = (4, 8, 16, 64)
 ROUTING_ROTATE = 20
 FP8_ROTATE = 5
 

@@ -13,7 +13,7 @@ centred second moment), in float64 with
 numpy, so a reader can check it against the pages by eye. Sources:
 
 * "RedFuser episode transcript" (podcast.do-not-panic.com, episode of
-  2026-10-13), cues 5, 9, 11, 15, 19, 21, 29, 31, 33, 39, 47.
+  2026-10-13), cues 5, 9, 11, 15, 19, 21, 29, 31, 33, 39, 41, 47, 55.
 * "RedFuser episode visual explainer" (same site, /viz/), the widgets
   "Online softmax, step by step", "Rescale the output accumulator too" and
   "Merging partial states across blocks (FlashDecoding-style)".

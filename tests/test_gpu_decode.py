@@ -76,7 +76,7 @@ def decode_config():
     return q, k, v, q.to(DEV), k.to(DEV), v.to(DEV)
 
 
-@pytest.mark.parametrize("S", [1, 4, 16, 64])
+@pytest.mark.parametrize("S", [1, 4, 8, 16, 64])
 def test_decode_config_sampled(decode_config, S):
     q, k, v, qd, kd, vd = decode_config
     print_case(test="decode_full", S=S)
