@@ -27,7 +27,8 @@
 //    been crossed.
 //  * Workgroups of one (batch, head) are placed on the same XCD (workgroups are
 //    dealt round-robin to the 8 XCDs), so its K/V stream is shared in one L2.
-//    Causal blocks are issued longest first.
+//    A causal workgroup takes query blocks u and nqb-1-u one after the other,
+//    so all causal workgroups have the same number of key tiles.
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
 
@@ -65,19 +66,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   // [K0 | K1 | V0 | V1], 16 KB each.
   __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
 
-  // Workgroup -> (batch*head, query block).
+  // Workgroup -> (batch*head, work unit). A unit is one query block, or for
+  // causal attention the pair of blocks u and nqb-1-u (the longer first), so
+  // every unit has the same number of key tiles.
+  const int nunits = CAUSAL ? (nqb + 1) / 2 : nqb;
   const int id = blockIdx.x;
-  int bh, qb;
+  int bh, unit;
   if ((BH & 7) == 0) {
     const int x = id & 7, j = id >> 3;
-    bh = (j / nqb) * 8 + x;
-    qb = j % nqb;
+    bh = (j / nunits) * 8 + x;
+    unit = j % nunits;
   } else {
-    bh = id / nqb;
-    qb = id % nqb;
+    bh = id / nunits;
+    unit = id % nunits;
   }
-  if (CAUSAL) qb = nqb - 1 - qb;
   const int b = bh / Hq, h = bh - b * Hq, hk = h / (Hq / Hkv);
+  const int npass = (CAUSAL && 2 * unit + 1 != nqb) ? 2 : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+  const int qb = !CAUSAL ? unit : (pass == 0 ? nqb - 1 - unit : unit);
   const int q0 = qb * BM;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -335,6 +341,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     }
     if (lse && g == 0) lse[(size_t)bh * Lq + qrow] = (m_c + __log2f(l_run)) * kLn2;
   }
+  }  // pass
 }
 
 }  // namespace
@@ -346,7 +353,7 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
   const int nqb = (Lq + BM - 1) / BM;
   const int BH = B * Hq;
   const float c = scale * kLog2e;
-  dim3 grid(BH * nqb);
+  dim3 grid(BH * (causal ? (nqb + 1) / 2 : nqb));
   auto qq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(k);
   auto vv = static_cast<const uint16_t*>(v);

@@ -52,6 +52,8 @@ def test_fp32_ragged_gqa(shape):
         ((1, 2, 2, 300, 300, 128), False),     # several blocks and a ragged tail
         ((1, 2, 2, 300, 300, 128), True),
         ((2, 4, 2, 257, 257, 128), True),      # GQA 2:1, tail of one row
+        ((1, 2, 2, 512, 512, 128), True),      # four query blocks: pairs (3, 0) and (2, 1)
+        ((1, 1, 1, 640, 640, 128), True),      # five blocks: pairs and a lone middle block
         ((1, 4, 1, 130, 200, 128), False),     # Lq != Lk, GQA 4:1
         ((1, 1, 1, 5, 3, 128), False),         # fewer keys than a tile
         ((1, 1, 1, 1, 1, 128), True),
