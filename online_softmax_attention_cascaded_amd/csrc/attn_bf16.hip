@@ -67,8 +67,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
 
   // Workgroup -> (batch*head, work unit). A unit is one query block, or for
-  // causal attention the pair of blocks u and nqb-1-u (the longer first), so
-  // every unit has the same number of key tiles.
+  // causal attention the pair of blocks u and nqb-1-u, so every unit has the
+  // same number of key tiles. The longer block goes first, so the workgroups
+  // of one head start on the same key tiles together and share them in L2
+  // (the shorter block second re-reads its tiles: about 360 MB per launch
+  // against 270 MB of operands; the other order fetched 477 MB).
   const int nunits = CAUSAL ? (nqb + 1) / 2 : nqb;
   const int id = blockIdx.x;
   int bh, unit;

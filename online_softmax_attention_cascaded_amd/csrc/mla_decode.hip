@@ -138,7 +138,8 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_kernel(
   const int ro = rrow * kRowBytes + DL * 2 + 16 * ((lane & 7) ^ rope_swz(rrow & 31));
   auto issue = [&](int t) {
     char* st = smem + (t % NST) * kStageBytes;
-    const int soff = __builtin_amdgcn_readfirstlane((k0 + STEP * t) * kRowBytes);
+    // steps past the segment point past the cache: zeros, no memory traffic
+    const int soff = __builtin_amdgcn_readfirstlane((t < nsteps ? k0 + STEP * t : Lk) * kRowBytes);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (4 * wave + i) * 1024), 16, lo[i],
@@ -155,9 +156,10 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_kernel(
   float m_c = kNegInf, l_run = 0.f;  // reference max (exp2 units) and denominator
   float m_true = kNegInf;             // the segment's true max, exp2 units
 
-  // Keys past the segment are still loaded (rows of the next segment, or
-  // zeros past the cache) and masked; steps past the segment load nothing
-  // useful but keep every wave's load count per step constant.
+  // Keys of the last step that lie past the segment are still loaded (rows
+  // of the next segment, or zeros past the cache) and masked; steps past the
+  // segment load zeros from past the cache, which keeps every wave's load
+  // count per step constant.
   issue(0);
   issue(1);
   issue(2);
