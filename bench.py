@@ -257,9 +257,12 @@ def main():
         events.append(step(i, True))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    samples = {n: [] for n in names}
     for ev in events:
         for n, a, b in zip(names, ev[:-1], ev[1:]):
-            times[n] += a.elapsed_time(b) / 1e3  # seconds
+            dt = a.elapsed_time(b) / 1e3  # seconds
+            times[n] += dt
+            samples[n].append(dt)
     per = {n: times[n] / args.steps for n in names}  # seconds per launch group
 
     pre_tflops = prefill_flops(False) / per["prefill"] / 1e12
@@ -318,6 +321,8 @@ def main():
                                "note": "quantiser + GEMM time, GEMM flops only"},
         },
         "us_per_launch": {n: round(per[n] * 1e6, 2) for n in names},
+        "us_spread": {n: {"min": round(min(v) * 1e6, 2), "median": round(sorted(v)[len(v) // 2] * 1e6, 2),
+                          "max": round(max(v) * 1e6, 2)} for n, v in samples.items()},
         "tokens_per_s": {
             "prefill": PREFILL["B"] * PREFILL["L"] / per["prefill"],
             "decode": DECODE["B"] / per[f"decode_s{best_S}"],
