@@ -314,11 +314,13 @@ def main():
                        "by_segments": {str(S): round(x, 1) for S, x in dec.items()},
                        "traffic": traffic.get("decode_split")},
             "routing": {"bound": "hbm", "achieved": round(rout_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(rout_gbs / PEAK_HBM_GBS, 4)},
+                        "frac": round(rout_gbs / PEAK_HBM_GBS, 4), "traffic": traffic.get("softmax_topk")},
             "fp8_quant_gemm": {"bound": "mfma", "achieved": round(gemm_flops() / per["fp8"] / 1e12, 2),
                                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                                "frac": round(gemm_flops() / per["fp8"] / 1e12 / PEAK_FP8_TFLOPS, 4),
-                               "note": "quantiser + GEMM time, GEMM flops only"},
+                               "note": "quantiser + GEMM time, GEMM flops only",
+                               "traffic": (traffic["absmax_quant"] + traffic["gemm_fp8"]
+                                           if "absmax_quant" in traffic and "gemm_fp8" in traffic else None)},
         },
         "us_per_launch": {n: round(per[n] * 1e6, 2) for n in names},
         "us_spread": {n: {"min": round(min(v) * 1e6, 2), "median": round(sorted(v)[len(v) // 2] * 1e6, 2),
@@ -381,7 +383,9 @@ def main():
         "bound": "hbm", "segments": best_mla, "achieved": round(mla_bytes / mla_t[best_mla] / 1e9, 1),
         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(mla_bytes / mla_t[best_mla] / 1e9 / PEAK_HBM_GBS, 4),
         "by_segments": {str(S): round(mla_bytes / t / 1e9, 1) for S, t in mla_t.items()},
-        "note": "latent rows read once; split + merge timed together"}
+        "note": "latent rows read once; split + merge timed together",
+        "traffic": traffic.get("mla_decode_split"),
+        "traffic_note": "split kernel, mean over the timed segment counts; the merge reads the partials again"}
     del Mq, Mkv
     progress("multi-latent decode timed")
 
