@@ -77,7 +77,8 @@ def test_quantiser_every_bf16_pattern():
     assert len(bad) == 0, f"{len(bad)} codes differ, first {bad[:3].tolist()}"
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 64, 256), (300, 200, 512), (256, 512, 1024), (1, 3, 128)])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 256), (300, 200, 512), (256, 512, 1024), (1, 3, 128),
+                                   (40, 260, 8192)])   # largest supported K, ragged M and N
 def test_gemm_small(M, N, K):
     print_case(test="gemm_small", M=M, N=N, K=K)
     a, bsrc = inputs.quant_inputs(11, M, N, K)
