@@ -164,20 +164,19 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_kernel(
   issue(1);
   issue(2);
   for (int t = 0; t < nsteps; ++t) {
-    // Every wave is done with step t-1: its stage takes step t+3 at once,
-    // before anyone waits for step t, so three steps stay in flight.
+    // This wave's loads of step t have landed (those of steps t+1 and t+2 may
+    // stay in flight); after the barrier every wave's have, and every wave
+    // is done with step t-1, whose stage then takes step t+3.
+    if (wave < 4)
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     lds_barrier();
     issue(t + 3);
-    // loads of steps t+1 .. t+3 may stay in flight
-    if (wave < 4)
-      asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    lds_barrier();
     const char* st = smem + (t % NST) * kStageBytes;
 
-    // partial scores of keys 16 kt .. +15
-    // two independent accumulation chains (even and odd k-steps)
+    // partial scores of keys 16 kt .. +15, in two independent accumulation
+    // chains (even and odd k-steps)
     f32x4 sp0 = {0.f, 0.f, 0.f, 0.f}, sp1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 6; j += 2) {
