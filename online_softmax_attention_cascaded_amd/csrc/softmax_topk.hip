@@ -7,9 +7,11 @@
 // is the faster one whenever the reduced axis fits on chip, cue 45). Logits are
 // mapped to order-preserving unsigned keys, so ranking, ties and the wave
 // reductions are integer operations. Top-k is k rounds of: each lane's best
-// untaken key (lowest index among equals), a wavefront max by DPP within rows
-// of 16 lanes and a scalar max across the four rows, then the lowest expert
-// index among the lanes holding that key. Ranking by the fp32 logit is the
+// untaken key (lowest index among equals), a max over the lanes of the row by
+// DPP, then the lowest expert index among the lanes holding that key. For 256
+// experts and k <= 8 each lane sorts its candidates once, so a round only
+// compares list heads; otherwise a lane rescans its keys every round. Ranking
+// by the fp32 logit is the
 // same as ranking by probability because softmax is strictly increasing. The
 // top-1 logit is the row max, so the selected weights are exp(x_i - max),
 // divided by their own sum (renormalised) or by the row's denominator.
@@ -231,10 +233,110 @@ __global__ __launch_bounds__(256) void softmax_topk_e256_kernel(const float* __r
   }
 }
 
+// E = 256, k <= 8: the same mapping, but each lane first orders its 16
+// candidates once, so a round costs one comparison of the row's 16 list heads
+// instead of a rescan of 16 keys per lane. A candidate is the 64-bit value
+// key << 32 | (15 - slot): equal keys order by the lower slot, which is the
+// lower expert index within the lane. The two halves of a lane's 16 are sorted
+// by an 8-input network (19 comparators); the elementwise max of one sorted
+// half and the other reversed holds the lane's 8 best as a bitonic sequence,
+// which three merge stages sort. A lane supplies at most k <= 8 winners, so 8
+// entries suffice; the winning lane drops its head each round.
+__device__ __forceinline__ void cx_desc(uint64_t& a, uint64_t& b) {
+  const bool keep = a >= b;
+  const uint64_t hi = keep ? a : b, lo = keep ? b : a;
+  a = hi;
+  b = lo;
+}
+template <int OFF>
+__device__ __forceinline__ void sort8_desc(uint64_t (&v)[16]) {
+  constexpr int net[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6},
+                              {3, 7}, {0, 1}, {2, 3}, {4, 5}, {6, 7}, {2, 4}, {3, 5},
+                              {1, 4}, {3, 6}, {1, 2}, {3, 4}, {5, 6}};
+#pragma unroll
+  for (int c = 0; c < 19; ++c) cx_desc(v[OFF + net[c][0]], v[OFF + net[c][1]]);
+}
+
+__global__ __launch_bounds__(256) void softmax_topk_e256_k8_kernel(const float* __restrict__ logits,
+                                                                   int T, int k, int renorm,
+                                                                   float* __restrict__ weights,
+                                                                   int32_t* __restrict__ indices) {
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  // A row past T reads the last row (valid memory) and writes nothing; all 64
+  // lanes stay active for the DPP reductions.
+  const float* x = logits + (size_t)min(row, T - 1) * 256;
+
+  float xv[16];
+  uint64_t v[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x) + 16 * c + j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * c + e;
+      xv[t] = w[e];
+      v[t] = ((uint64_t)order_key(w[e]) << 32) | (uint64_t)(15 - t);
+    }
+  }
+  sort8_desc<0>(v);
+  sort8_desc<8>(v);
+  uint64_t s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = v[i] >= v[15 - i] ? v[i] : v[15 - i];
+#pragma unroll
+  for (int d = 4; d > 0; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & d) == 0) cx_desc(s[i], s[i + d]);
+
+  uint32_t top = 0, my_key = 0;
+  int my_idx = 0;
+  for (int r = 0; r < k; ++r) {
+    const uint32_t hk = (uint32_t)(s[0] >> 32);
+    const int slot = 15 - (int)(s[0] & 15u);
+    const uint32_t wk = row16_max_u32(hk);
+    const uint32_t mine = (hk == wk) ? (uint32_t)(64 * (slot >> 2) + 4 * j + (slot & 3)) : 0xffffffffu;
+    const uint32_t widx = row16_min_u32(mine);
+    const bool win = mine == widx;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) s[i] = win ? s[i + 1] : s[i];
+    s[7] = win ? 0ull : s[7];
+    if (r == 0) top = wk;
+    if (j == r) {
+      my_key = wk;
+      my_idx = (int)widx;
+    }
+  }
+
+  const float m = key_value(top);
+  const float e = (j < k) ? expf(key_value(my_key) - m) : 0.f;
+  float denom;
+  if (renorm) {
+    denom = row16_sum_f32(e);
+  } else {
+    float l = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) l += fast_exp2((xv[t] - m) * kLog2e);
+    denom = row16_sum_f32(l);
+  }
+  if (row < T && j < k) {
+    weights[(size_t)row * k + j] = e / denom;
+    indices[(size_t)row * k + j] = my_idx;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_softmax_topk(const float* logits, int T, int E, int k, int renormalize,
                                float* weights, int32_t* indices, hipStream_t stream) {
+#ifndef RF_TOPK_NO_SORTED
+  if (E == 256 && k <= 8) {
+    hipLaunchKernelGGL(softmax_topk_e256_k8_kernel, dim3((T + 15) / 16), dim3(256), 0, stream,
+                       logits, T, k, renormalize, weights, indices);
+    return hipGetLastError();
+  }
+#endif
   if (E == 256 && k <= 16) {
     hipLaunchKernelGGL(softmax_topk_e256_kernel, dim3((T + 15) / 16), dim3(256), 0, stream, logits,
                        T, k, renormalize, weights, indices);

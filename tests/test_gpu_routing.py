@@ -29,7 +29,7 @@ def test_routing_config(renormalize):
     _check(inputs.routing_inputs(3, 16384, 256), 8, renormalize)
 
 
-@pytest.mark.parametrize("E,k", [(4, 1), (4, 4), (64, 2), (128, 8), (256, 1), (256, 8), (256, 16), (256, 32), (512, 8), (1024, 16), (1000, 5)])
+@pytest.mark.parametrize("E,k", [(4, 1), (4, 4), (64, 2), (128, 8), (256, 1), (256, 2), (256, 5), (256, 7), (256, 8), (256, 9), (256, 16), (256, 32), (512, 8), (1024, 16), (1000, 5)])
 def test_routing_shapes(E, k):
     print_case(test="routing_shapes", E=E, k=k)
     _check(inputs.routing_inputs(9, 37, E), k, True)
@@ -40,17 +40,39 @@ def test_routing_ties(seed):
     """Logits drawn from four values: almost every selection is a tie."""
     _check(inputs.tie_heavy_logits(seed, 300, 256), 8, True)
     _check(inputs.tie_heavy_logits(seed, 300, 64), 8, False)
+    _check(inputs.tie_heavy_logits(seed, 300, 256), 8, False)
+    _check(inputs.tie_heavy_logits(seed, 300, 256), 3, True)
+
+
+@pytest.mark.parametrize("renormalize", [True, False])
+def test_routing_winners_in_one_slice(renormalize):
+    """256 experts: the kernel gives each of 16 lanes the experts 4 j + 64 c + e
+    (c, e < 4). Rows whose whole top-8 lies in one such set of 16, with equal
+    values among them, so one lane supplies every winner."""
+    import torch
+
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn((48, 256), generator=g)
+    for r in range(48):
+        j = r % 16
+        own = [4 * j + 64 * c + e for c in range(4) for e in range(4)]
+        vals = torch.tensor([9.0, 9.0, 8.5, 8.0, 8.0, 8.0, 7.5, 7.0, 6.5, 6.5, 6.0, 5.5, 5.0, 5.0, 4.5, 4.0])
+        perm = torch.randperm(16, generator=g)
+        x[r, own] = vals[perm]
+    _check(x, 8, renormalize)
+    _check(x, 5, renormalize)
 
 
 def test_routing_signed_zero_ties():
     """-0.0 and +0.0 are equal logits: the lower index goes first."""
     import torch
 
-    x = torch.zeros((8, 64))
-    x[:, ::2] = -0.0
-    x[:, 5] = 1.0
-    _check(x, 8, True)
-    _check(x, 8, False)
+    for E in (64, 256):
+        x = torch.zeros((8, E))
+        x[:, ::2] = -0.0
+        x[:, 5] = 1.0
+        _check(x, 8, True)
+        _check(x, 8, False)
 
 
 def test_routing_empty():
