@@ -25,7 +25,8 @@ namespace {
 // first, so equal values have equal keys).
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t u = __float_as_uint(x + 0.f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: all bits flipped; otherwise the sign bit set
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
@@ -34,9 +35,13 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 // DPP controls (gfx9): quad permutations, half-row and row mirrors.
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
+// Every pattern used here reads a lane of the same row, and every caller runs
+// with all 64 lanes active, so no source lane is out of range or disabled and
+// the bound-control zero fill never applies; with it set and no old value to
+// keep, the compiler folds the move into the max / min / add that consumes it.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
 // Max over the 64 lanes of the wave (result uniform).
@@ -233,15 +238,22 @@ __global__ __launch_bounds__(256) void softmax_topk_e256_kernel(const float* __r
   }
 }
 
-// E = 256, k <= 8: the same mapping, but each lane first orders its 16
-// candidates once, so a round costs one comparison of the row's 16 list heads
-// instead of a rescan of 16 keys per lane. A candidate is the 64-bit value
-// key << 32 | (15 - slot): equal keys order by the lower slot, which is the
-// lower expert index within the lane. The two halves of a lane's 16 are sorted
-// by an 8-input network (19 comparators); the elementwise max of one sorted
-// half and the other reversed holds the lane's 8 best as a bitonic sequence,
-// which three merge stages sort. A lane supplies at most k <= 8 winners, so 8
-// entries suffice; the winning lane drops its head each round.
+// E = 256, k <= 8: the same mapping, but each lane orders its 16 candidates
+// once, so a round costs one comparison of the row's 16 list heads instead of
+// a rescan of 16 keys per lane. A lane supplies at most k <= 8 winners, so its
+// best 8 suffice; the winning lane drops its head each round.
+//
+// Fast form: a candidate is its key with the low 4 bits replaced by 15 - slot,
+// sorted by a 63-comparator network of 32-bit max / min. Keys whose upper 28
+// bits differ keep their order; keys that agree there (equal keys included)
+// land next to each other, and if any lane of the wave has such a pair the
+// wave takes the exact form instead: 64-bit candidates key << 32 | (15 - slot)
+// (equal keys order by the lower slot, i.e. the lower expert index within the
+// lane), both halves sorted by a 19-comparator 8-input network, the
+// elementwise max of one half and the other reversed (the best 8 as a bitonic
+// sequence) sorted by three merge stages. The fast form recovers a head's low
+// key bits from a per-lane table before comparing across lanes, so the
+// cross-lane comparison is always on the exact key.
 __device__ __forceinline__ void cx_desc(uint64_t& a, uint64_t& b) {
   const bool keep = a >= b;
   const uint64_t hi = keep ? a : b, lo = keep ? b : a;
@@ -256,6 +268,23 @@ __device__ __forceinline__ void sort8_desc(uint64_t (&v)[16]) {
 #pragma unroll
   for (int c = 0; c < 19; ++c) cx_desc(v[OFF + net[c][0]], v[OFF + net[c][1]]);
 }
+// Batcher's odd-even merge sort of 16 (descending).
+__device__ __forceinline__ void sort16_desc(uint32_t (&v)[16]) {
+  constexpr int net[63][2] = {
+      {0, 1},   {2, 3},   {0, 2},   {1, 3},   {1, 2},   {4, 5},   {6, 7},   {4, 6},   {5, 7},
+      {5, 6},   {0, 4},   {2, 6},   {2, 4},   {1, 5},   {3, 7},   {3, 5},   {1, 2},   {3, 4},
+      {5, 6},   {8, 9},   {10, 11}, {8, 10},  {9, 11},  {9, 10},  {12, 13}, {14, 15}, {12, 14},
+      {13, 15}, {13, 14}, {8, 12},  {10, 14}, {10, 12}, {9, 13},  {11, 15}, {11, 13}, {9, 10},
+      {11, 12}, {13, 14}, {0, 8},   {4, 12},  {4, 8},   {2, 10},  {6, 14},  {6, 10},  {2, 4},
+      {6, 8},   {10, 12}, {1, 9},   {5, 13},  {5, 9},   {3, 11},  {7, 15},  {7, 11},  {3, 5},
+      {7, 9},   {11, 13}, {1, 2},   {3, 4},   {5, 6},   {7, 8},   {9, 10},  {11, 12}, {13, 14}};
+#pragma unroll
+  for (int c = 0; c < 63; ++c) {
+    const uint32_t a = v[net[c][0]], b = v[net[c][1]];
+    v[net[c][0]] = max(a, b);
+    v[net[c][1]] = min(a, b);
+  }
+}
 
 __global__ __launch_bounds__(256) void softmax_topk_e256_k8_kernel(const float* __restrict__ logits,
                                                                    int T, int k, int renorm,
@@ -268,44 +297,79 @@ __global__ __launch_bounds__(256) void softmax_topk_e256_k8_kernel(const float* 
   const float* x = logits + (size_t)min(row, T - 1) * 256;
 
   float xv[16];
-  uint64_t v[16];
+  uint32_t key[16];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x) + 16 * c + j);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = 4 * c + e;
-      xv[t] = w[e];
-      v[t] = ((uint64_t)order_key(w[e]) << 32) | (uint64_t)(15 - t);
+      xv[4 * c + e] = w[e];
+      key[4 * c + e] = order_key(w[e]);
     }
   }
-  sort8_desc<0>(v);
-  sort8_desc<8>(v);
-  uint64_t s[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s[i] = v[i] >= v[15 - i] ? v[i] : v[15 - i];
-#pragma unroll
-  for (int d = 4; d > 0; d >>= 1)
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if ((i & d) == 0) cx_desc(s[i], s[i + d]);
+  // expert index of slot t of this lane
+  auto expert = [&](int t) { return (uint32_t)(64 * (t >> 2) + 4 * j + (t & 3)); };
 
   uint32_t top = 0, my_key = 0;
   int my_idx = 0;
-  for (int r = 0; r < k; ++r) {
-    const uint32_t hk = (uint32_t)(s[0] >> 32);
-    const int slot = 15 - (int)(s[0] & 15u);
-    const uint32_t wk = row16_max_u32(hk);
-    const uint32_t mine = (hk == wk) ? (uint32_t)(64 * (slot >> 2) + 4 * j + (slot & 3)) : 0xffffffffu;
-    const uint32_t widx = row16_min_u32(mine);
-    const bool win = mine == widx;
+  uint32_t cd[16], low_a = 0, low_b = 0;
 #pragma unroll
-    for (int i = 0; i < 7; ++i) s[i] = win ? s[i + 1] : s[i];
-    s[7] = win ? 0ull : s[7];
-    if (r == 0) top = wk;
-    if (j == r) {
-      my_key = wk;
-      my_idx = (int)widx;
+  for (int t = 0; t < 16; ++t) {
+    cd[t] = (key[t] & ~0xFu) | (uint32_t)(15 - t);
+    if (t < 8)
+      low_a |= (key[t] & 0xFu) << (4 * t);
+    else
+      low_b |= (key[t] & 0xFu) << (4 * (t - 8));
+  }
+  sort16_desc(cd);
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) near |= (cd[i] ^ cd[i + 1]) < 16u;
+
+  if (!__any(near)) {
+    for (int r = 0; r < k; ++r) {
+      const uint32_t h = cd[0];
+      const int slot = 15 - (int)(h & 15u);
+      const uint32_t lw = slot < 8 ? low_a : low_b;
+      const uint32_t hk = (h & ~0xFu) | ((lw >> (4 * (slot & 7))) & 0xFu);
+      const uint32_t wk = row16_max_u32(hk);
+      const uint32_t widx = row16_min_u32(hk == wk ? expert(slot) : 0xffffffffu);
+      const bool win = hk == wk && expert(slot) == widx;
+#pragma unroll
+      for (int i = 0; i < 7; ++i) cd[i] = win ? cd[i + 1] : cd[i];
+      if (r == 0) top = wk;
+      if (j == r) {
+        my_key = wk;
+        my_idx = (int)widx;
+      }
+    }
+  } else {
+    uint64_t v[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) v[t] = ((uint64_t)key[t] << 32) | (uint64_t)(15 - t);
+    sort8_desc<0>(v);
+    sort8_desc<8>(v);
+    uint64_t s8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s8[i] = v[i] >= v[15 - i] ? v[i] : v[15 - i];
+#pragma unroll
+    for (int d = 4; d > 0; d >>= 1)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if ((i & d) == 0) cx_desc(s8[i], s8[i + d]);
+    for (int r = 0; r < k; ++r) {
+      const uint32_t hk = (uint32_t)(s8[0] >> 32);
+      const int slot = 15 - (int)(s8[0] & 15u);
+      const uint32_t wk = row16_max_u32(hk);
+      const uint32_t widx = row16_min_u32(hk == wk ? expert(slot) : 0xffffffffu);
+      const bool win = hk == wk && expert(slot) == widx;
+#pragma unroll
+      for (int i = 0; i < 7; ++i) s8[i] = win ? s8[i + 1] : s8[i];
+      if (r == 0) top = wk;
+      if (j == r) {
+        my_key = wk;
+        my_idx = (int)widx;
+      }
     }
   }
 
