@@ -61,6 +61,32 @@ def test_routing_winners_in_one_slice(renormalize):
         x[r, own] = vals[perm]
     _check(x, 8, renormalize)
     _check(x, 5, renormalize)
+    # distinct values: the same rows without equal keys
+    for r in range(48):
+        j = r % 16
+        own = [4 * j + 64 * c + e for c in range(4) for e in range(4)]
+        x[r, own] = 4.0 + 0.25 * torch.randperm(16, generator=g).float()
+    _check(x, 8, renormalize)
+
+
+@pytest.mark.parametrize("renormalize", [True, False])
+def test_routing_one_ulp_neighbours(renormalize):
+    """256 experts: the leading logits are consecutive fp32 values (keys that
+    differ only in their lowest bits), placed at random experts, so some rows
+    hold such neighbours inside one lane's set of experts and others only
+    across lanes."""
+    import torch
+
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    ladder = [np.float32(5.0)]
+    for _ in range(11):
+        ladder.append(np.nextafter(ladder[-1], np.float32(np.inf)))
+    for r in range(64):
+        cols = rng.choice(256, size=12, replace=False)
+        x[r, cols] = np.array(ladder, np.float32)[rng.permutation(12)]
+    _check(torch.from_numpy(x), 8, renormalize)
+    _check(torch.from_numpy(x), 3, renormalize)
 
 
 def test_routing_signed_zero_ties():
