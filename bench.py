@@ -491,6 +491,77 @@ def main():
         "achieved": round(gemm_tflops, 1), "unit": "TFLOP/s",
         "prefill_frac_of_it": round(pre_tflops / gemm_tflops, 4)}
     progress("vendor bf16 GEMM timed for context")
+
+    # Measured ceilings beside the published peaks: the MFMA loops of
+    # rf_peak_mfma on operand data like the workloads' (512 workgroups, two
+    # waves per SIMD), with the shader clock they ran at; for HBM, a 2 GiB read
+    # stream (rf_peak_read) and a 1 GiB device copy (read + write bytes).
+    khz = rf.rf_wall_clock_khz()
+    blocks = 512
+    measured = {}
+    for kind, name, iters, per_mfma in ((rf.RF_PEAK_BF16, "bf16", 8192, 32768),
+                                        (rf.RF_PEAK_FP8, "fp8", 4096, 131072)):
+        if kind == rf.RF_PEAK_BF16:
+            vals = torch.randn((blocks * 256, 128), device=dev, generator=gen).to(torch.bfloat16)
+        else:
+            vals = (torch.randn((blocks * 256, 256), device=dev, generator=gen) * 100).clamp(
+                -448, 448).to(torch.float8_e4m3fn)
+        src = vals.view(torch.uint8).reshape(blocks * 256, 256)
+        pout = torch.empty(blocks * 4, device=dev)
+        clk = torch.zeros((blocks, 2), dtype=torch.int64, device=dev)
+        for _ in range(2):
+            rf.rf_peak_mfma(kind, src, iters, pout, clk)
+        e0.record()
+        for _ in range(5):
+            rf.rf_peak_mfma(kind, src, iters, pout, clk)
+        e1.record()
+        torch.cuda.synchronize()
+        t_pk = e0.elapsed_time(e1) / 1e3 / 5
+        ck = clk.cpu().double()
+        ghz = float((ck[:, 0] / ck[:, 1]).median()) * khz / 1e6
+        measured[name] = (blocks * 4 * iters * 8 * per_mfma / t_pk / 1e12, ghz)
+        del vals, src, pout, clk
+    cp_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    for _ in range(3):
+        cp_dst.copy_(cp_src)
+    e0.record()
+    for _ in range(10):
+        cp_dst.copy_(cp_src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * (1 << 30) / (e0.elapsed_time(e1) / 1e3 / 10) / 1e9
+    del cp_dst
+    rd_src = torch.cat([cp_src, cp_src])   # 2 GiB, well past the 256 MB last-level cache
+    del cp_src
+    # 32768 workgroups of 64 KB each: many short-lived workgroups kept the
+    # stream fastest (2048 / 8192 / 32768 workgroups: 6.0 / 6.7 / 6.9 TB/s)
+    rd_out = torch.empty(32768, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        rf.rf_peak_read(rd_src, 32768, rd_out)
+    e0.record()
+    for _ in range(10):
+        rf.rf_peak_read(rd_src, 32768, rd_out)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 2.0 * (1 << 30) / (e0.elapsed_time(e1) / 1e3 / 10) / 1e9
+    del rd_src, rd_out
+    bf_tf, bf_ghz = measured["bf16"]
+    f8_tf, f8_ghz = measured["fp8"]
+    mfma_kind = "MFMA loop (rf_peak_mfma) on N(0,1)-like operands, 2 waves per SIMD"
+    result["roofline"]["measured_peak"] = {
+        "kind": "bf16 " + mfma_kind, "achieved": round(bf_tf, 1), "unit": "TFLOP/s",
+        "clock_ghz": round(bf_ghz, 3), "frac": round(pre_tflops / bf_tf, 4)}
+    result["rooflines"]["prefill_causal"]["measured_peak_frac"] = round(pre_c_tflops / bf_tf, 4)
+    fp8_tf = gemm_flops() / per["fp8"] / 1e12
+    result["rooflines"]["fp8_quant_gemm"]["measured_peak"] = {
+        "kind": "fp8 e4m3 " + mfma_kind, "achieved": round(f8_tf, 1), "unit": "TFLOP/s",
+        "clock_ghz": round(f8_ghz, 3), "frac": round(fp8_tf / f8_tf, 4)}
+    result["rooflines"]["decode"]["measured_peak"] = {
+        "kind": "HBM read stream of 2 GiB (rf_peak_read, 32768 workgroups)",
+        "achieved": round(read_gbs, 1), "unit": "GB/s", "frac": round(dec_gbs / read_gbs, 4),
+        "copy_1GiB": {"achieved": round(copy_gbs, 1), "unit": "GB/s (read + write bytes, torch copy)"}}
+    progress("measured MFMA and copy ceilings timed")
     if not args.no_cpu_baseline:
         progress("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline()

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 5
+#define RF_ABI_VERSION 6
 
 typedef enum {
   RF_OK = 0,
@@ -254,6 +254,48 @@ rf_status rf_absmax_quant_gemm_fp8(const void* a, const uint8_t* b, const float*
 rf_status rf_absmax_quant_gemm_fp8_running(const void* a, const uint8_t* b, const float* b_scale,
                                            int M, int N, int K, float* a_scale, void* c,
                                            hipStream_t stream);
+
+/*
+ * Measurement support (not a step of the path): the matrix-core rate this GPU
+ * sustains and the shader clock it runs at, against which the MFMA-bound
+ * kernels above are compared. The clock depends on the operand data (the
+ * board's power limit lowers it as more bits switch), so the loop multiplies
+ * data the caller supplies.
+ *
+ * rf_peak_mfma -- `blocks` workgroups of 4 waves; each lane loads 8 operand
+ * vectors, then runs `iters` iterations of 8 MFMAs (operands j and (j+3) % 8)
+ * onto 4 independent accumulators, with no memory traffic in the loop.
+ *   kind RF_PEAK_BF16: v_mfma_f32_32x32x16_bf16, 32768 flops per wave-MFMA
+ *   kind RF_PEAK_FP8:  v_mfma_f32_32x32x64_f8f6f4 on e4m3, 131072 flops
+ *   flops per call = blocks * 4 * iters * 8 * (flops per wave-MFMA)
+ *   src   [blocks * 256][256] bytes, 32-byte aligned: lane t of workgroup b
+ *         reads row 256 b + t; operand j is at byte 32 j (bf16: 8 values in
+ *         its first 16 bytes; fp8: 32 e4m3 codes)
+ *   out   [blocks * 4] fp32, written: per wave, the sum of all its
+ *         accumulator elements (a checksum of the products)
+ *   clock [blocks * 2] uint64 or NULL: per workgroup, shader-clock cycles and
+ *         constant-rate ticks from its start to its end (rf_wall_clock_khz
+ *         gives the tick rate; cycles / ticks * rate = shader clock)
+ *   1 <= blocks <= 65536, 1 <= iters <= 2^20.
+ */
+typedef enum { RF_PEAK_BF16 = 0, RF_PEAK_FP8 = 1 } rf_peak_kind;
+rf_status rf_peak_mfma(int kind, const void* src, int blocks, int iters, float* out,
+                       unsigned long long* clock, hipStream_t stream);
+
+/*
+ * rf_peak_read -- HBM read stream: `blocks` workgroups of 256 threads read
+ * `bytes` of `src` once in 16-byte loads, eight independent loads in flight
+ * per thread, walking the buffer in grid-strided rounds. out[b] = XOR of the
+ * 32-bit words workgroup b read, so the XOR over out is the XOR of every word
+ * of src whatever the order.
+ *   src 16-byte aligned, bytes % 16 == 0;  out [blocks] uint32;
+ *   1 <= blocks <= 65536.
+ */
+rf_status rf_peak_read(const void* src, long long bytes, int blocks, uint32_t* out,
+                       hipStream_t stream);
+
+/* Rate of the constant-rate counter of the current device, in kHz. */
+rf_status rf_wall_clock_khz(int* khz);
 
 /* Human-readable name of a status code (static storage). */
 const char* rf_status_string(rf_status s);

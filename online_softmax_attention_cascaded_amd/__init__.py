@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     RF_FUSE_NONE,
     RF_FUSE_THREAD,
     RF_FUSE_WAVE,
+    RF_PEAK_BF16,
+    RF_PEAK_FP8,
     RFError,
     attn_decode,
     attn_decode_partials,
@@ -30,10 +32,13 @@ from .binding import (  # noqa: F401
     rf_attn_fwd,
     rf_merge_states,
     rf_mla_decode_split,
+    rf_peak_mfma,
+    rf_peak_read,
     rf_row_inertia,
     rf_row_variance,
     rf_softmax,
     rf_softmax_topk,
+    rf_wall_clock_khz,
     softmax,
     softmax_topk,
 )

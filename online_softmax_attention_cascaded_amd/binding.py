@@ -19,6 +19,7 @@ from .build import LIB_PATH
 RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_LAUNCH = 0, 1, 2, 3
 RF_F32, RF_BF16 = 0, 1
 RF_FUSE_NONE, RF_FUSE_THREAD, RF_FUSE_WAVE, RF_FUSE_BLOCK = 0, 1, 2, 3
+RF_PEAK_BF16, RF_PEAK_FP8 = 0, 1
 
 # Every entry point of the C ABI with its argument types.
 _P = ctypes.c_void_p
@@ -36,6 +37,9 @@ SIGNATURES = {
     "rf_absmax_quant_fp8": [_P, _I, _I, _P, _P, _P],
     "rf_absmax_quant_gemm_fp8": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
     "rf_absmax_quant_gemm_fp8_running": [_P, _P, _P, _I, _I, _I, _P, _P, _P],
+    "rf_peak_mfma": [_I, _P, _I, _I, _P, _P, _P],
+    "rf_peak_read": [_P, ctypes.c_longlong, _I, _P, _P],
+    "rf_wall_clock_khz": [ctypes.POINTER(ctypes.c_int)],
     "rf_status_string": [_I],
     "rf_last_error": [],
     "rf_abi_version": [],
@@ -195,6 +199,37 @@ def rf_absmax_quant_gemm_fp8_running(a, b_q, b_scale, a_scale, c):
     N = b_q.shape[0]
     _check(lib().rf_absmax_quant_gemm_fp8_running(_ptr(a), _ptr(b_q), _ptr(b_scale), M, N, K,
                                                   _ptr(a_scale), _ptr(c), _stream(a)))
+
+
+def rf_peak_mfma(kind, src, iters, out, clock=None):
+    """Measurement loop (not a step of the path): src is a uint8 tensor
+    [blocks * 256, 256]; out fp32 [blocks * 4]; clock int64 [blocks, 2] or None."""
+    _dev(src, out, clock)
+    if src.dtype != torch.uint8 or src.dim() != 2 or src.shape[1] != 256 or src.shape[0] % 256:
+        raise ValueError("src must be uint8 [blocks * 256, 256]")
+    blocks = src.shape[0] // 256
+    if out.dtype != torch.float32 or out.numel() != 4 * blocks:
+        raise ValueError("out must be fp32 with 4 values per workgroup")
+    if clock is not None and (clock.dtype != torch.int64 or clock.numel() != 2 * blocks):
+        raise ValueError("clock must be int64 [blocks, 2]")
+    _check(lib().rf_peak_mfma(int(kind), _ptr(src), blocks, int(iters), _ptr(out), _ptr(clock),
+                              _stream(src)))
+
+
+def rf_peak_read(src, blocks, out):
+    """HBM read stream (not a step of the path): src any contiguous device
+    tensor (16-byte multiple); out int32 [blocks] gets per-workgroup XORs."""
+    _dev(src, out)
+    nbytes = src.numel() * src.element_size()
+    if out.dtype != torch.int32 or out.numel() != blocks:
+        raise ValueError("out must be int32 [blocks]")
+    _check(lib().rf_peak_read(_ptr(src), nbytes, int(blocks), _ptr(out), _stream(src)))
+
+
+def rf_wall_clock_khz():
+    khz = ctypes.c_int(0)
+    _check(lib().rf_wall_clock_khz(ctypes.byref(khz)))
+    return khz.value
 
 
 # ---------------------------------------------------------------- allocating helpers

@@ -160,6 +160,40 @@ rf_status rf_softmax_topk(const float* logits, int T, int E, int k, int renormal
                      "rf_softmax_topk");
 }
 
+rf_status rf_peak_mfma(int kind, const void* src, int blocks, int iters, float* out,
+                       unsigned long long* clock, hipStream_t stream) {
+  RF_REQUIRE(kind == RF_PEAK_BF16 || kind == RF_PEAK_FP8, RF_ERR_INVALID_ARG,
+             "rf_peak_mfma: unknown kind %d", kind);
+  RF_REQUIRE(blocks >= 1 && blocks <= 65536, RF_ERR_INVALID_ARG,
+             "rf_peak_mfma: blocks=%d outside 1..65536", blocks);
+  RF_REQUIRE(iters >= 1 && iters <= (1 << 20), RF_ERR_INVALID_ARG,
+             "rf_peak_mfma: iters=%d outside 1..2^20", iters);
+  RF_REQUIRE(src && out, RF_ERR_INVALID_ARG, "rf_peak_mfma: null pointer");
+  RF_REQUIRE(aligned(src, 32) && aligned(out, 4) && aligned(clock, 8), RF_ERR_INVALID_ARG,
+             "rf_peak_mfma: misaligned pointer");
+  return from_launch(rf::launch_peak_mfma(kind, src, blocks, iters, out, clock, stream),
+                     "rf_peak_mfma");
+}
+
+rf_status rf_peak_read(const void* src, long long bytes, int blocks, uint32_t* out,
+                       hipStream_t stream) {
+  RF_REQUIRE(bytes >= 0 && bytes % 16 == 0, RF_ERR_INVALID_ARG,
+             "rf_peak_read: bytes=%lld must be a non-negative multiple of 16", bytes);
+  RF_REQUIRE(blocks >= 1 && blocks <= 65536, RF_ERR_INVALID_ARG,
+             "rf_peak_read: blocks=%d outside 1..65536", blocks);
+  RF_REQUIRE(out && (src || bytes == 0), RF_ERR_INVALID_ARG, "rf_peak_read: null pointer");
+  RF_REQUIRE(aligned(src, 16) && aligned(out, 4), RF_ERR_INVALID_ARG, "rf_peak_read: misaligned pointer");
+  return from_launch(rf::launch_peak_read(src, bytes, blocks, out, stream), "rf_peak_read");
+}
+
+rf_status rf_wall_clock_khz(int* khz) {
+  RF_REQUIRE(khz, RF_ERR_INVALID_ARG, "rf_wall_clock_khz: null pointer");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+  return from_launch(e, "rf_wall_clock_khz");
+}
+
 rf_status rf_softmax(const float* x, int T, int E, int level, float* work, float* y,
                      hipStream_t stream) {
   RF_REQUIRE(T >= 0 && E >= 0, RF_ERR_INVALID_ARG, "rf_softmax: negative size");

@@ -50,4 +50,9 @@ hipError_t launch_gemm_fp8_scaled(const uint8_t* a_q, const float* a_scale, cons
 hipError_t launch_gemm_fp8_running(const void* a, const uint8_t* b_q, const float* b_scale, int M,
                                    int N, int K, float* a_scale, void* c, hipStream_t stream);
 
+hipError_t launch_peak_mfma(int kind, const void* src, int blocks, int iters, float* out,
+                            unsigned long long* clk, hipStream_t stream);
+hipError_t launch_peak_read(const void* src, long long bytes, int blocks, uint32_t* out,
+                            hipStream_t stream);
+
 }  // namespace rf

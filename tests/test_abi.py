@@ -55,7 +55,7 @@ def test_argument_counts_match_header():
 
 
 def test_status_helpers(lib):
-    assert lib.rf_abi_version() == 5
+    assert lib.rf_abi_version() == 6
     assert lib.rf_status_string(OK) == b"RF_OK"
     assert lib.rf_status_string(INVALID) == b"RF_ERR_INVALID_ARG"
     assert lib.rf_status_string(UNSUPPORTED) == b"RF_ERR_UNSUPPORTED"
@@ -229,3 +229,24 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(4, 256)
     with pytest.raises(ValueError):
         binding.softmax_topk(x, 8)
+
+
+def test_peak_validation(lib):
+    f = lib.rf_peak_mfma
+    assert f(2, FAKE, 4, 8, FAKE, None, None) == INVALID          # unknown kind
+    assert f(0, FAKE, 0, 8, FAKE, None, None) == INVALID
+    assert f(0, FAKE, 65537, 8, FAKE, None, None) == INVALID
+    assert f(1, FAKE, 4, 0, FAKE, None, None) == INVALID
+    assert f(1, FAKE, 4, (1 << 20) + 1, FAKE, None, None) == INVALID
+    assert f(0, None, 4, 8, FAKE, None, None) == INVALID
+    assert f(0, FAKE, 4, 8, None, None, None) == INVALID
+    assert f(0, ctypes.c_void_p(0x10010), 4, 8, FAKE, None, None) == INVALID   # src not 32-byte aligned
+    assert f(0, FAKE, 4, 8, FAKE, MISALIGNED, None) == INVALID
+    assert lib.rf_last_error().startswith(b"rf_peak_mfma")
+    assert lib.rf_wall_clock_khz(None) == INVALID
+    g = lib.rf_peak_read
+    assert g(FAKE, 100, 4, FAKE, None) == INVALID                 # bytes % 16
+    assert g(FAKE, -16, 4, FAKE, None) == INVALID
+    assert g(FAKE, 1024, 0, FAKE, None) == INVALID
+    assert g(FAKE, 1024, 4, None, None) == INVALID
+    assert g(MISALIGNED, 1024, 4, FAKE, None) == INVALID
