@@ -510,6 +510,38 @@ def main():
         "prefill_frac_of_it": round(pre_tflops / gemm_tflops, 4)}
     progress("vendor bf16 GEMM timed for context")
 
+    # The vendor's attention on the same prefill inputs: torch's
+    # scaled_dot_product_attention restricted to its flash backend (on ROCm,
+    # AOTriton kernels), which raises instead of falling back to the unfused
+    # math path. Reported beside the roofline; null if the backend is missing.
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    vendor_attn = {}
+    for causal in (False, True):
+        try:
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                for _ in range(3):
+                    torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=scale)
+                e0.record()
+                for _ in range(10):
+                    torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=scale)
+                e1.record()
+                torch.cuda.synchronize()
+            vendor_attn[causal] = prefill_flops(causal) / (e0.elapsed_time(e1) / 1e3 / 10) / 1e12
+        except RuntimeError as ex:
+            progress(f"torch flash attention unavailable: {ex}")
+            vendor_attn[causal] = None
+    va = vendor_attn[False]
+    result["roofline"]["vendor_attention"] = {
+        "kind": "torch scaled_dot_product_attention, flash backend only, same inputs",
+        "achieved": None if va is None else round(va, 1), "unit": "TFLOP/s",
+        "speedup": None if va is None else round(pre_tflops / va, 3)}
+    vc = vendor_attn[True]
+    result["rooflines"]["prefill_causal"]["vendor_attention"] = {
+        "achieved": None if vc is None else round(vc, 1), "unit": "TFLOP/s",
+        "speedup": None if vc is None else round(pre_c_tflops / vc, 3)}
+    progress("vendor attention timed for context")
+
     # Measured ceilings beside the published peaks: the MFMA loops of
     # rf_peak_mfma on operand data like the workloads' (512 workgroups, two
     # waves per SIMD), with the shader clock they ran at; for HBM, a 2 GiB read
