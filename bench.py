@@ -612,6 +612,63 @@ def main():
         "achieved": round(read_gbs, 1), "unit": "GB/s", "frac": round(dec_gbs / read_gbs, 4),
         "copy_1GiB": {"achieved": round(copy_gbs, 1), "unit": "GB/s (read + write bytes, torch copy)"}}
     progress("measured MFMA and copy ceilings timed")
+
+    # The vendor libraries on the same inputs, row by row (torch's own kernels;
+    # none of them is part of the path). Short launches run back to back behind
+    # a spin kernel, as for the routing roofline.
+    def vendor_time(fn, n, warm=3):
+        for _ in range(warm):
+            fn(0)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(2_000_000)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    def torch_routing(i):
+        p = torch.softmax(logits[i % ROUTING_ROTATE], dim=-1)
+        wv, iv = torch.topk(p, R["k"], dim=-1)
+        return wv / wv.sum(dim=-1, keepdim=True), iv
+
+    t_vr = vendor_time(torch_routing, 2 * ROUTING_ROTATE)
+    vendor = {"routing": {"kind": "torch softmax, topk, renormalise", "us_per_launch": round(t_vr * 1e6, 2),
+                          "speedup": round(t_vr / t_rout_b2b, 3)}}
+    sm_v, var_v = {}, {}
+    for E in SOFTMAX_E:
+        T = SOFTMAX_VALUES // E
+        xs = inputs.softmax_inputs(6, T, E).to(dev)
+        t_v = vendor_time(lambda i: torch.softmax(xs, dim=-1), 10)
+        sm_v[f"E{E}"] = {"GBs": round(8.0 * T * E / t_v / 1e9, 1),
+                         "speedup": round(t_v / sm_rates[(E, "block")][0], 3)}
+        xm, _ = (t.to(dev) for t in inputs.moment_inputs(8, T, E))
+        t_v = vendor_time(lambda i: torch.var_mean(xm, dim=-1, unbiased=False), 10)
+        best = min(mom[("variance", E, ln)][0] for ln in levels if ln != "unfused")
+        var_v[f"E{E}"] = {"GBs": round(4.0 * T * E / t_v / 1e9, 1), "speedup": round(t_v / best, 3)}
+        del xs, xm
+    vendor["softmax_rows"] = {"kind": "torch.softmax over the same rows; speedup of the block-level form",
+                              "by_row_length": sm_v}
+    vendor["variance"] = {"kind": "torch.var_mean(unbiased=False); speedup of the best fused form",
+                          "by_row_length": var_v}
+    try:
+        a8 = aq.view(torch.float8_e4m3fn)
+        b8 = bq.view(torch.float8_e4m3fn)
+        rf.rf_absmax_quant_fp8(a_bufs[0], aq, sa)
+        sa2, sb2 = sa.view(-1, 1), bs.view(1, -1)
+        t_vg = vendor_time(lambda i: torch._scaled_mm(a8, b8.t(), scale_a=sa2, scale_b=sb2,
+                                                      out_dtype=torch.bfloat16), 10)
+        vendor["fp8_gemm"] = {"kind": "torch._scaled_mm with row and column scales (GEMM only) on this "
+                                      "path's quantised operands",
+                              "us_per_launch": round(t_vg * 1e6, 2),
+                              "tflops": round(gemm_flops() / t_vg / 1e12, 1),
+                              "this_path_quant_plus_gemm_us": round(per["fp8"] * 1e6, 2)}
+    except RuntimeError as ex:
+        progress(f"torch scaled FP8 GEMM unavailable: {ex}")
+        vendor["fp8_gemm"] = None
+    result["vendor"] = vendor
+    progress("vendor kernels timed for context")
     if not args.no_cpu_baseline:
         progress("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline()
