@@ -78,7 +78,8 @@ def test_quantiser_every_bf16_pattern():
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 64, 256), (300, 200, 512), (256, 512, 1024), (1, 3, 128),
-                                   (40, 260, 8192)])   # largest supported K, ragged M and N
+                                   (40, 260, 8192),    # largest supported K, ragged M and N
+                                   (520, 264, 256), (72, 776, 384)])   # N % 8 == 0, partial tiles
 def test_gemm_small(M, N, K):
     print_case(test="gemm_small", M=M, N=N, K=K)
     a, bsrc = inputs.quant_inputs(11, M, N, K)
