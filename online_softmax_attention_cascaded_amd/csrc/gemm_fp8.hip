@@ -7,23 +7,24 @@
 // the per-lane layout of the MFMA operands. Workgroup tile 256 x 256 (one per
 // CU at 4096^2), sixteen waves of 64 x 64, four per SIMD, so one wave's wait
 // on an LDS read or a barrier is covered by the MFMAs of the others. K is
-// staged 64 bytes at a time through a ring of four LDS stages filled by buffer
-// loads straight into LDS (no staging registers; rows past M or N read as 0),
-// up to three stages ahead of the MFMAs. A step reads its fragments from its
-// own stage (B blocks first, then A), so a stage is refilled one step after
-// it was read. The 16-byte chunks of each 64-byte LDS row are XOR-swizzled by
-// the row so the operand reads of consecutive lanes use distinct banks. The
-// scales are applied once, in the epilogue, which stages the bf16 tile in LDS
-// so that every row of C is written as whole 512-byte segments.
+// staged 128 bytes at a time through two LDS stages filled by buffer loads
+// straight into LDS (no staging registers; rows past M or N read as 0): while
+// the MFMAs of one stage run, the loads of the next fill the other, with one
+// barrier per 128 bytes of K. A step reads its fragments from its own stage,
+// in two k-substeps of 64 bytes. The 16-byte chunks of each 128-byte LDS row
+// are XOR-swizzled by the row so the operand reads of consecutive lanes use
+// distinct banks. The scales are applied once, in the epilogue, which stages
+// the bf16 tile in LDS so that every row of C is written as whole 512-byte
+// segments.
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
 
 namespace rf {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kStages = 4;
-constexpr int kTileBytes = BM * BK;          // 16 KB per operand per stage
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int kStages = 2;
+constexpr int kTileBytes = BM * BK;          // 32 KB per operand per stage
 constexpr int kStageBytes = 2 * kTileBytes;  // A + B
 constexpr int kGroupM = 4;                   // tile rows per band of the tile order
 constexpr int kThreads = 1024;               // 16 waves
@@ -31,10 +32,11 @@ constexpr int kThreads = 1024;               // 16 waves
 typedef __attribute__((address_space(3))) void lds_void;
 
 // ds_read_b128 serves 16 lanes per LDS cycle (64 banks of 4 bytes). The operand
-// read of 16 consecutive lanes touches 16 consecutive rows: rows r and r + 4
-// share banks unless their chunks differ, which the XOR with (row >> 2) & 3
-// guarantees over any 16 aligned rows.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// read of 16 consecutive lanes touches 16 consecutive rows at one logical
+// chunk. A 128-byte row spans half the banks, so rows r and r + 1 sit in
+// different halves; the XOR with (row >> 1) & 7 gives the 8 row pairs of any
+// 16 aligned rows 8 different chunks, i.e. distinct 4-bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * BK + ((chunk ^ swz(row)) << 4);
 }
@@ -72,47 +74,51 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const uint8_t* __
   tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // HBM -> LDS: per stage and operand, wave w fills one 1 KB block, rows
-  // 16 w .. 16 w + 15; lane l writes row 16 w + l / 4 at physical chunk l % 4,
-  // so it fetches the logical chunk that the swizzle puts there.
+  // HBM -> LDS: per stage and operand, wave w fills two 1 KB blocks (8 rows of
+  // 128 B each); lane l writes row 8 b + l / 8 of block b at physical chunk
+  // l % 8, so it fetches the logical chunk that the swizzle puts there.
   const __amdgpu_buffer_rsrc_t ars = make_rsrc(aq + (size_t)m0 * K, (uint32_t)(min(BM, M - m0) * K));
   const __amdgpu_buffer_rsrc_t brs = make_rsrc(bq + (size_t)n0 * K, (uint32_t)(min(BN, N - n0) * K));
-  int voff;
-  {
-    const int row = 16 * wave + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz(row);
-    voff = row * K + 16 * chunk;
+  int voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * (2 * wave + i) + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    voff[i] = row * K + 16 * chunk;
   }
   auto issue = [&](int kt) {
     char* st = smem + (kt % kStages) * kStageBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void*)(st + wave * 1024), 16, voff, kt * BK, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void*)(st + kTileBytes + wave * 1024), 16, voff,
-                                             kt * BK, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void*)(st + (2 * wave + i) * 1024), 16, voff[i],
+                                               kt * BK, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void*)(st + kTileBytes + (2 * wave + i) * 1024), 16,
+                                               voff[i], kt * BK, 0, 0);
+    }
   };
   // Wait until this wave's loads of a stage have landed while `newer` later
-  // stages (2 loads each) may stay in flight.
+  // stages (4 loads each) may stay in flight.
   auto wait_stage = [](int newer) {
-    if (newer >= 3)
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if (newer == 2)
+    if (newer >= 1)
       asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if (newer == 1)
-      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
   // Fragments of a step, read from that step's stage: B blocks j (rows
-  // wn*64 + 32 j + li) and A blocks i (rows wm*64 + 32 i + li), each 32 bytes of
-  // K (logical chunks 2 half and 2 half + 1) read as two 16-byte halves.
+  // wn*64 + 32 j + li) and A blocks i (rows wm*64 + 32 i + li); in k-substep q
+  // each is 32 bytes of K (logical chunks 4 q + 2 half and 4 q + 2 half + 1)
+  // read as two 16-byte halves.
   const int half = lane >> 5, li = lane & 31;
-  int bo[2][2], ao[2][2];
+  int bo[2][2][2], ao[2][2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) bo[j][h] = kTileBytes + lds_off(wn * 64 + 32 * j + li, 2 * half + h);
+    for (int j = 0; j < 2; ++j) bo[q][j][h] = kTileBytes + lds_off(wn * 64 + 32 * j + li, 4 * q + 2 * half + h);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ao[i][h] = lds_off(wm * 64 + 32 * i + li, 2 * half + h);
+    for (int i = 0; i < 2; ++i) ao[q][i][h] = lds_off(wm * 64 + 32 * i + li, 4 * q + 2 * half + h);
   }
   auto rd = [](const char* st, int off) { return *reinterpret_cast<const u32x4*>(st + off); };
   auto frag = [](const u32x4& p0, const u32x4& p1) {
@@ -130,27 +136,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const uint8_t* __
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   const int nk = K / BK;
-  for (int s = 0; s < 3 && s < nk; ++s) issue(s);
+  issue(0);
   for (int kt = 0; kt < nk; ++kt) {
-    // This wave's loads of stage kt have landed (kt+1 and kt+2 may be in flight);
-    // after the barrier everyone's have, and everyone is done with stage kt-1,
-    // whose slot takes stage kt+3.
-    wait_stage(min(2, nk - 1 - kt));
+    // This wave's loads of stage kt have landed; after the barrier everyone's
+    // have, and everyone is done with stage kt-1, whose slot takes stage kt+1.
+    wait_stage(0);
     lds_barrier();
-    if (kt + 3 < nk) issue(kt + 3);
+    if (kt + 1 < nk) issue(kt + 1);
     const char* st = smem + (kt % kStages) * kStageBytes;
-    u32x4 b0[2], b1[2], a[2][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      b0[h] = rd(st, bo[0][h]);
-      a[0][h] = rd(st, ao[0][h]);
-      b1[h] = rd(st, bo[1][h]);
-      a[1][h] = rd(st, ao[1][h]);
-    }
+    for (int q = 0; q < 2; ++q) {
+      u32x4 b0[2], b1[2], a[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      acc[i][0] = mfma_fp8(frag(b0[0], b0[1]), frag(a[i][0], a[i][1]), acc[i][0]);
-      acc[i][1] = mfma_fp8(frag(b1[0], b1[1]), frag(a[i][0], a[i][1]), acc[i][1]);
+      for (int h = 0; h < 2; ++h) {
+        b0[h] = rd(st, bo[q][0][h]);
+        a[0][h] = rd(st, ao[q][0][h]);
+        b1[h] = rd(st, bo[q][1][h]);
+        a[1][h] = rd(st, ao[q][1][h]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        acc[i][0] = mfma_fp8(frag(b0[0], b0[1]), frag(a[i][0], a[i][1]), acc[i][0]);
+        acc[i][1] = mfma_fp8(frag(b1[0], b1[1]), frag(a[i][0], a[i][1]), acc[i][1]);
+      }
     }
   }
 
@@ -213,3 +221,4 @@ hipError_t launch_gemm_fp8_scaled(const uint8_t* a_q, const float* a_scale, cons
 }
 
 }  // namespace rf
+
