@@ -284,10 +284,10 @@ rf_status rf_peak_mfma(int kind, const void* src, int blocks, int iters, float* 
 
 /*
  * rf_peak_read -- HBM read stream: `blocks` workgroups of 256 threads read
- * `bytes` of `src` once in 16-byte loads, eight independent loads in flight
- * per thread, walking the buffer in grid-strided rounds. out[b] = XOR of the
- * 32-bit words workgroup b read, so the XOR over out is the XOR of every word
- * of src whatever the order.
+ * `bytes` of `src` once in 16-byte loads, workgroup b its own contiguous share,
+ * eight independent loads in flight per thread. out[b] = XOR of the 32-bit
+ * words workgroup b read, so the XOR over out is the XOR of every word of src
+ * whatever the order.
  *   src 16-byte aligned, bytes % 16 == 0;  out [blocks] uint32;
  *   1 <= blocks <= 65536.
  */

@@ -66,21 +66,24 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(const uint8_t* __restric
   }
 }
 
-// HBM read stream: every thread keeps 8 independent 16-byte loads in flight
-// (32 KB per workgroup), walking the buffer in grid-strided rounds; the XOR of
-// every 32-bit word it read is folded per workgroup, so the result does not
-// depend on the order. Many short-lived workgroups (a few rounds each) keep
-// the stream fastest.
+// HBM read stream: workgroup b reads its own contiguous share of the buffer,
+// each thread keeping 8 independent 16-byte loads in flight (32 KB per
+// workgroup), so every load instruction covers 1 KB of consecutive bytes and a
+// wave walks its share in order; the XOR of every 32-bit word read is folded
+// per workgroup, so the result does not depend on the order. (Grid-strided
+// rounds, with a wave's successive loads far apart, ran 6.0-6.9 TB/s against
+// 7.0-7.1 for this pattern.)
 __global__ __launch_bounds__(256) void peak_read_kernel(const u32x4* __restrict__ src, long long n16,
                                                         uint32_t* __restrict__ out) {
-  const long long stride = (long long)gridDim.x * 256;
+  const long long per = (n16 + gridDim.x - 1) / gridDim.x;
+  const long long lo = min(n16, (long long)blockIdx.x * per), hi = min(n16, lo + per);
   u32x4 x = {0u, 0u, 0u, 0u};
-  for (long long base = (long long)blockIdx.x * 256 + threadIdx.x; base < n16; base += 8 * stride) {
+  for (long long base = lo + threadIdx.x; base < hi; base += 8 * 256) {
     u32x4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const long long i = base + u * stride;
-      v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+      const long long i = base + 256 * u;
+      v[u] = i < hi ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) x ^= v[u];
