@@ -371,37 +371,48 @@ def main():
         "unit": "TFLOP/s", "frac": round(gemm_flops() / t_run / 1e12 / PEAK_FP8_TFLOPS, 4),
         "note": "single kernel: running per-row scale, A quantised inside the K loop"}
     # Split-KV decode over a shared latent cache (multi-latent attention),
-    # partial states + merge, at each segment count. Algorithmic bytes: the
+    # partial states + merge, at each segment count, as two launches and as
+    # one (the last workgroup of each group merges). Algorithmic bytes: the
     # latent rows once (B * Lk * 576 * 2) plus q and O.
     Mq, Mkv = (t.to(dev) for t in inputs.mla_inputs(7, MLA["B"], MLA["H"], MLA["Lk"]))
     mla_bytes = (MLA["B"] * MLA["Lk"] * MLA["dqk"] * 2 + MLA["B"] * MLA["H"] * MLA["dqk"] * 2
                  + MLA["B"] * MLA["H"] * MLA["dv"] * 2)
     mo = torch.empty((MLA["B"], MLA["H"], MLA["dv"]), dtype=torch.bfloat16, device=dev)
     mlse = torch.empty((MLA["B"], MLA["H"]), device=dev)
-    mla_t = {}
+    counters = torch.zeros(MLA["B"] * MLA["H"] // 16, dtype=torch.int32, device=dev)
+    mla_t, mla_one = {}, {}
     for S in MLA_SEGMENTS:
         pm = torch.empty((MLA["B"], MLA["H"], S), device=dev)
         pl = torch.empty_like(pm)
         pa = torch.empty((MLA["B"], MLA["H"], S, MLA["dv"]), device=dev)
 
-        def mla_call():
+        def mla_two_launches():
             rf.rf_mla_decode_split(Mq, Mkv, pm, pl, pa, 1 / math.sqrt(MLA["dqk"]))
             rf.rf_merge_states(pm, pl, pa, mo, mlse)
-        for _ in range(10):
-            mla_call()
-        e0.record()
-        for _ in range(args.steps):
-            mla_call()
-        e1.record()
-        torch.cuda.synchronize()
-        mla_t[S] = e0.elapsed_time(e1) / 1e3 / args.steps
+
+        def mla_fused():
+            rf.rf_mla_decode(Mq, Mkv, pm, pl, pa, counters, mo, mlse, 1 / math.sqrt(MLA["dqk"]))
+        for fn, store in ((mla_two_launches, mla_t), (mla_fused, mla_one)):
+            for _ in range(10):
+                fn()
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            store[S] = e0.elapsed_time(e1) / 1e3 / args.steps
     best_mla = min(mla_t, key=mla_t.get)
     result["us_per_launch"].update({f"mla_decode_s{S}": round(t * 1e6, 2) for S, t in mla_t.items()})
+    result["us_per_launch"].update({f"mla_decode_one_launch_s{S}": round(t * 1e6, 2)
+                                    for S, t in mla_one.items()})
     result["rooflines"]["mla_decode"] = {
         "bound": "hbm", "segments": best_mla, "achieved": round(mla_bytes / mla_t[best_mla] / 1e9, 1),
         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(mla_bytes / mla_t[best_mla] / 1e9 / PEAK_HBM_GBS, 4),
         "by_segments": {str(S): round(mla_bytes / t / 1e9, 1) for S, t in mla_t.items()},
-        "note": "latent rows read once; split + merge timed together",
+        "one_launch_by_segments": {str(S): round(mla_bytes / t / 1e9, 1) for S, t in mla_one.items()},
+        "note": ("latent rows read once; split + merge as two launches. One launch (rf_mla_decode, "
+                 "last workgroup merges) is slower here: each workgroup's agent-scope release is an "
+                 "L2 write-back, and one workgroup folds all S states of its group"),
         "traffic": traffic.get("mla_decode_split"),
         "traffic_note": "split kernel, mean over the timed segment counts; the merge reads the partials again"}
     del Mq, Mkv

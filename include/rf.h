@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 6
+#define RF_ABI_VERSION 7
 
 typedef enum {
   RF_OK = 0,
@@ -130,6 +130,29 @@ rf_status rf_merge_states(const float* part_m, const float* part_l, const float*
 rf_status rf_mla_decode_split(const void* q, const void* kv, float* part_m, float* part_l,
                               float* part_acc, int B, int H, int Lk, int Dqk, int Dv, int S,
                               float scale, hipStream_t stream);
+
+/*
+ * rf_mla_decode -- rf_mla_decode_split and the merge of its S partial states
+ * (the rule of rf_merge_states, transcript cue 21) in one launch: each
+ * workgroup writes its partial state as rf_mla_decode_split does, makes it
+ * visible device-wide and counts itself in on its (sequence, head group)'s
+ * counter; the workgroup that completes the count merges that group's S
+ * states, writes O and lse, and sets the counter back to 0.
+ *
+ *   q, kv, part_m, part_l, part_acc, B, H, Lk, Dqk, Dv, S, scale: as for
+ *           rf_mla_decode_split (the partial states are written too).
+ *   counters [B * H / 16] int32, caller-owned, 4-byte aligned: all 0 before
+ *           the first call; every call that returns RF_OK and runs to
+ *           completion leaves them 0. Calls that share a counters array must
+ *           not run at the same time.
+ *   o       [B, H, 512] in out_dt (RF_BF16 or RF_F32), 16-byte aligned;
+ *   lse     [B, H] fp32 (natural log) or NULL.
+ * Publishing a state across the 8 XCDs costs an L2 write-back per workgroup,
+ * so on MI355X this measured slower than the two launches for S = 8 .. 32.
+ */
+rf_status rf_mla_decode(const void* q, const void* kv, float* part_m, float* part_l, float* part_acc,
+                        int32_t* counters, rf_dtype out_dt, void* o, float* lse, int B, int H, int Lk,
+                        int Dqk, int Dv, int S, float scale, hipStream_t stream);
 
 /*
  * rf_softmax_topk -- MoE routing: per row of logits, softmax then top-k

@@ -31,6 +31,7 @@ from .binding import (  # noqa: F401
     rf_attn_decode_split,
     rf_attn_fwd,
     rf_merge_states,
+    rf_mla_decode,
     rf_mla_decode_split,
     rf_peak_mfma,
     rf_peak_read,

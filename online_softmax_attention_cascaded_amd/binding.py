@@ -30,6 +30,7 @@ SIGNATURES = {
     "rf_attn_decode_split": [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
     "rf_merge_states": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
     "rf_mla_decode_split": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
+    "rf_mla_decode": [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
     "rf_softmax_topk": [_P, _I, _I, _I, _I, _P, _P, _P],
     "rf_softmax": [_P, _I, _I, _I, _P, _P, _P],
     "rf_row_variance": [_P, _I, _I, _I, _P, _P, _P],
@@ -137,6 +138,21 @@ def rf_mla_decode_split(q, kv, part_m, part_l, part_acc, scale):
     S, Dv = part_acc.shape[2], part_acc.shape[3]
     _check(lib().rf_mla_decode_split(_ptr(q), _ptr(kv), _ptr(part_m), _ptr(part_l), _ptr(part_acc),
                                      B, H, Lk, Dqk, Dv, S, float(scale), _stream(q)))
+
+
+def rf_mla_decode(q, kv, part_m, part_l, part_acc, counters, o, lse, scale):
+    """Split and merge in one launch; counters int32 [B * H / 16], zero on entry
+    and left zero."""
+    _dev(q, kv, part_m, part_l, part_acc, counters, o, lse)
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
+        raise ValueError("rf_mla_decode takes bf16 q and latent rows")
+    if counters.dtype != torch.int32:
+        raise ValueError("counters must be int32")
+    B, H, Dqk = q.shape
+    Lk = kv.shape[1]
+    S, Dv = part_acc.shape[2], part_acc.shape[3]
+    _check(lib().rf_mla_decode(_ptr(q), _ptr(kv), _ptr(part_m), _ptr(part_l), _ptr(part_acc), _ptr(counters),
+                               _dtype_code(o), _ptr(o), _ptr(lse), B, H, Lk, Dqk, Dv, S, float(scale), _stream(q)))
 
 
 def rf_merge_states(part_m, part_l, part_acc, o, lse):
@@ -265,12 +281,19 @@ def attn_decode(q, k, v, scale, S, out_dtype=torch.bfloat16):
     return o, lse, parts
 
 
-def mla_decode(q, kv, scale, S, dv=512, out_dtype=torch.bfloat16):
-    """Split-KV decode over a shared latent cache, then the merge of the partials."""
+def mla_decode(q, kv, scale, S, dv=512, out_dtype=torch.bfloat16, fused=False):
+    """Split-KV decode over a shared latent cache, then the merge of the
+    partials: two launches, or one (rf_mla_decode) with fused=True."""
     B, H, _ = q.shape
     part_m = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     part_l = torch.empty_like(part_m)
     part_acc = torch.empty((B, H, S, dv), dtype=torch.float32, device=q.device)
+    if fused:
+        counters = torch.zeros(B * H // 16, dtype=torch.int32, device=q.device)
+        o = torch.empty((B, H, dv), dtype=out_dtype, device=q.device)
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        rf_mla_decode(q, kv, part_m, part_l, part_acc, counters, o, lse, scale)
+        return o, lse, (part_m, part_l, part_acc)
     rf_mla_decode_split(q, kv, part_m, part_l, part_acc, scale)
     o, lse = merge_states(part_m, part_l, part_acc, out_dtype=out_dtype)
     return o, lse, (part_m, part_l, part_acc)

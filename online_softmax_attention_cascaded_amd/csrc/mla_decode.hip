@@ -52,11 +52,81 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8_t& a, const bf16x8_t& b, co
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Fused merge. Every workgroup of a (sequence, head group) makes its partial
+// state visible device-wide and counts itself in; the one that completes the
+// count merges the group's S states with the rescale-and-add rule (each state
+// moved to the common max, weight 0 for an empty one), writes O = acc / l and
+// lse = m + ln l, and returns the counter to zero for the next call.
+__device__ __forceinline__ void merge_if_last(int* __restrict__ counters, int* s_last, int cidx, int S,
+                                              int H, int b, int hg, const float* __restrict__ part_m,
+                                              const float* __restrict__ part_l,
+                                              const float* __restrict__ part_acc, void* __restrict__ o,
+                                              float* __restrict__ lse, int out_bf16) {
+  // One wave publishes for the workgroup. Every wave first waits until the L2
+  // has acknowledged its own stores of the state (the barrier alone does not
+  // wait for them); thread 0's agent-scope release, an L2 write-back costly
+  // enough to issue once per workgroup rather than once per wave, then covers
+  // them all, and only the last workgroup pays the acquire (an L2 invalidate)
+  // before reading the states.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const bool last =
+        __hip_atomic_fetch_add(counters + cidx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *s_last = last;
+  }
+  __syncthreads();
+  if (!*s_last) return;
+  // 16 heads x 512 columns: thread t takes head t / 32, columns 16 (t % 32) .. + 15.
+  const int t = threadIdx.x, head = hg * 16 + (t >> 5), c0 = 16 * (t & 31);
+  const size_t r0 = ((size_t)b * H + head) * S;
+  float m = kNegInf, l = 0.f;
+  f32x4 acc[4] = {};
+#pragma unroll 4
+  for (int si = 0; si < S; ++si) {
+    const float ms = part_m[r0 + si], ls = part_l[r0 + si];
+    const f32x4* as = reinterpret_cast<const f32x4*>(part_acc + (r0 + si) * DL + c0);
+    const float mn = fmaxf(m, ms);
+    const float wa = (m == kNegInf) ? 0.f : fast_exp2((m - mn) * kLog2e);
+    const float wb = (ms == kNegInf) ? 0.f : fast_exp2((ms - mn) * kLog2e);
+    l = l * wa + ls * wb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = acc[i] * wa + as[i] * wb;
+    m = mn;
+  }
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  const size_t orow = ((size_t)b * H + head) * DL + c0;
+  if (out_bf16) {
+    u32x4 w[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = acc[i] * inv;
+      w[i >> 1][2 * (i & 1)] = pack_bf16x2(v[0], v[1]);
+      w[i >> 1][2 * (i & 1) + 1] = pack_bf16x2(v[2], v[3]);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(o) + orow);
+    dst[0] = w[0];
+    dst[1] = w[1];
+  } else {
+    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = acc[i] * inv;
+  }
+  if (lse && (t & 31) == 0) lse[(size_t)b * H + head] = (m == kNegInf) ? kNegInf : m + logf(l);
+  if (t == 0) counters[cidx] = 0;
+}
+
 __global__ __launch_bounds__(512, 1) void mla_decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, float* __restrict__ part_m,
     float* __restrict__ part_l, float* __restrict__ part_acc, int H, int Lk, int S, int seg_len,
-    float c) {
+    float c, int* __restrict__ counters, void* __restrict__ o, float* __restrict__ lse, int out_bf16) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  // Flag of the fused merge, in the stage memory: written only after the last
+  // stage has been consumed. (A second LDS object would make the compiler
+  // wait for every pending buffer-to-LDS load before each LDS read.)
+  int* const s_last = reinterpret_cast<int*>(smem);
   const int ngroups = H >> 4;
   const int hg = blockIdx.x % ngroups;
   const int s = (blockIdx.x / ngroups) % S;
@@ -77,6 +147,9 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_kernel(
       part_m[prow] = kNegInf;
       part_l[prow] = 0.f;
     }
+    if (counters)
+      merge_if_last(counters, s_last, b * ngroups + hg, S, H, b, hg, part_m, part_l, part_acc, o, lse,
+                    out_bf16);
     return;
   }
   const int nsteps = (k1 - k0 + STEP - 1) / STEP;
@@ -274,18 +347,22 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_kernel(
     part_m[prow] = m_true * kLn2;
     part_l[prow] = l_run;
   }
+  if (counters)
+    merge_if_last(counters, s_last, b * ngroups + hg, S, H, b, hg, part_m, part_l, part_acc, o, lse,
+                  out_bf16);
 }
 
 }  // namespace
 
 hipError_t launch_mla_decode_split(const void* q, const void* kv, float* part_m, float* part_l,
                                    float* part_acc, int B, int H, int Lk, int S, float scale,
+                                   int* counters, void* o, float* lse, int out_bf16,
                                    hipStream_t stream) {
   const int seg_len = (Lk + S - 1) / S;
   const dim3 grid(B * S * (H / 16));
   hipLaunchKernelGGL(mla_decode_split_kernel, grid, dim3(512), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), part_m,
-                     part_l, part_acc, H, Lk, S, seg_len, scale * kLog2e);
+                     part_l, part_acc, H, Lk, S, seg_len, scale * kLog2e, counters, o, lse, out_bf16);
   return hipGetLastError();
 }
 

@@ -98,6 +98,32 @@ rf_status rf_attn_decode_split(rf_dtype dt, const void* q, const void* k, const 
                      "rf_attn_decode_split");
 }
 
+namespace {
+
+// Arguments shared by rf_mla_decode_split and rf_mla_decode; `fn` names the
+// caller in the error text.
+rf_status check_mla(const char* fn, const void* q, const void* kv, float* part_m, float* part_l,
+                    float* part_acc, int B, int H, int Lk, int Dqk, int Dv, int S, float scale) {
+  RF_REQUIRE(Lk >= 1, RF_ERR_INVALID_ARG, "%s: Lk must be >= 1", fn);
+  RF_REQUIRE(Dv >= 1 && Dv <= Dqk, RF_ERR_INVALID_ARG, "%s: value width %d must be in 1..%d", fn, Dv, Dqk);
+  RF_REQUIRE(q && kv && part_m && part_l && part_acc, RF_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  RF_REQUIRE(aligned(q, 16) && aligned(kv, 16) && aligned(part_acc, 16) && aligned(part_m, 4) &&
+                 aligned(part_l, 4),
+             RF_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  RF_REQUIRE(scale == scale, RF_ERR_INVALID_ARG, "%s: scale is NaN", fn);
+  RF_REQUIRE(Dqk == 576 && Dv == 512, RF_ERR_UNSUPPORTED,
+             "%s: widths %d/%d (need 576 for keys, 512 for values)", fn, Dqk, Dv);
+  RF_REQUIRE(H % 16 == 0 && H <= 128, RF_ERR_UNSUPPORTED,
+             "%s: H=%d (need a multiple of 16, at most 128)", fn, H);
+  RF_REQUIRE((long long)(Lk + 96) * Dqk * 2 < (1LL << 31), RF_ERR_UNSUPPORTED,
+             "%s: one sequence's cache reaches 2 GiB", fn);
+  RF_REQUIRE((long long)B * S * (H / 16) < (1LL << 31) && (long long)B * H * S * Dv < (1LL << 40),
+             RF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  return ok();
+}
+
+}  // namespace
+
 rf_status rf_mla_decode_split(const void* q, const void* kv, float* part_m, float* part_l,
                               float* part_acc, int B, int H, int Lk, int Dqk, int Dv, int S,
                               float scale, hipStream_t stream) {
@@ -105,25 +131,32 @@ rf_status rf_mla_decode_split(const void* q, const void* kv, float* part_m, floa
              "rf_mla_decode_split: negative size");
   RF_REQUIRE(S >= 1, RF_ERR_INVALID_ARG, "rf_mla_decode_split: S=%d must be >= 1", S);
   if ((long long)B * H == 0) return ok();
-  RF_REQUIRE(Lk >= 1, RF_ERR_INVALID_ARG, "rf_mla_decode_split: Lk must be >= 1");
-  RF_REQUIRE(Dv >= 1 && Dv <= Dqk, RF_ERR_INVALID_ARG,
-             "rf_mla_decode_split: value width %d must be in 1..%d", Dv, Dqk);
-  RF_REQUIRE(q && kv && part_m && part_l && part_acc, RF_ERR_INVALID_ARG,
-             "rf_mla_decode_split: null tensor pointer");
-  RF_REQUIRE(aligned(q, 16) && aligned(kv, 16) && aligned(part_acc, 16) && aligned(part_m, 4) &&
-                 aligned(part_l, 4),
-             RF_ERR_INVALID_ARG, "rf_mla_decode_split: misaligned pointer");
-  RF_REQUIRE(scale == scale, RF_ERR_INVALID_ARG, "rf_mla_decode_split: scale is NaN");
-  RF_REQUIRE(Dqk == 576 && Dv == 512, RF_ERR_UNSUPPORTED,
-             "rf_mla_decode_split: widths %d/%d (need 576 for keys, 512 for values)", Dqk, Dv);
-  RF_REQUIRE(H % 16 == 0 && H <= 128, RF_ERR_UNSUPPORTED,
-             "rf_mla_decode_split: H=%d (need a multiple of 16, at most 128)", H);
-  RF_REQUIRE((long long)(Lk + 96) * Dqk * 2 < (1LL << 31), RF_ERR_UNSUPPORTED,
-             "rf_mla_decode_split: one sequence's cache reaches 2 GiB");
-  RF_REQUIRE((long long)B * S * (H / 16) < (1LL << 31) && (long long)B * H * S * Dv < (1LL << 40),
-             RF_ERR_INVALID_ARG, "rf_mla_decode_split: problem too large");
-  return from_launch(rf::launch_mla_decode_split(q, kv, part_m, part_l, part_acc, B, H, Lk, S, scale, stream),
+  const rf_status st = check_mla("rf_mla_decode_split", q, kv, part_m, part_l, part_acc, B, H, Lk, Dqk,
+                                 Dv, S, scale);
+  if (st != RF_OK) return st;
+  return from_launch(rf::launch_mla_decode_split(q, kv, part_m, part_l, part_acc, B, H, Lk, S, scale,
+                                                 nullptr, nullptr, nullptr, 0, stream),
                      "rf_mla_decode_split");
+}
+
+rf_status rf_mla_decode(const void* q, const void* kv, float* part_m, float* part_l, float* part_acc,
+                        int32_t* counters, rf_dtype out_dt, void* o, float* lse, int B, int H, int Lk,
+                        int Dqk, int Dv, int S, float scale, hipStream_t stream) {
+  RF_REQUIRE(out_dt == RF_F32 || out_dt == RF_BF16, RF_ERR_INVALID_ARG,
+             "rf_mla_decode: unknown dtype %d", (int)out_dt);
+  RF_REQUIRE(B >= 0 && H >= 0 && Lk >= 0 && Dqk >= 0 && Dv >= 0, RF_ERR_INVALID_ARG,
+             "rf_mla_decode: negative size");
+  RF_REQUIRE(S >= 1, RF_ERR_INVALID_ARG, "rf_mla_decode: S=%d must be >= 1", S);
+  if ((long long)B * H == 0) return ok();
+  const rf_status st = check_mla("rf_mla_decode", q, kv, part_m, part_l, part_acc, B, H, Lk, Dqk, Dv,
+                                 S, scale);
+  if (st != RF_OK) return st;
+  RF_REQUIRE(counters && o, RF_ERR_INVALID_ARG, "rf_mla_decode: null counters or output");
+  RF_REQUIRE(aligned(counters, 4) && aligned(o, 16) && aligned(lse, 4), RF_ERR_INVALID_ARG,
+             "rf_mla_decode: misaligned pointer");
+  return from_launch(rf::launch_mla_decode_split(q, kv, part_m, part_l, part_acc, B, H, Lk, S, scale,
+                                                 counters, o, lse, out_dt == RF_BF16 ? 1 : 0, stream),
+                     "rf_mla_decode");
 }
 
 rf_status rf_merge_states(const float* part_m, const float* part_l, const float* part_acc,

@@ -26,6 +26,7 @@ hipError_t launch_merge_states(const float* part_m, const float* part_l, const f
 
 hipError_t launch_mla_decode_split(const void* q, const void* kv, float* part_m, float* part_l,
                                    float* part_acc, int B, int H, int Lk, int S, float scale,
+                                   int* counters, void* o, float* lse, int out_bf16,
                                    hipStream_t stream);
 
 hipError_t launch_softmax_topk(const float* logits, int T, int E, int k, int renormalize,

@@ -55,7 +55,7 @@ def test_argument_counts_match_header():
 
 
 def test_status_helpers(lib):
-    assert lib.rf_abi_version() == 6
+    assert lib.rf_abi_version() == 7
     assert lib.rf_status_string(OK) == b"RF_OK"
     assert lib.rf_status_string(INVALID) == b"RF_ERR_INVALID_ARG"
     assert lib.rf_status_string(UNSUPPORTED) == b"RF_ERR_UNSUPPORTED"
@@ -148,6 +148,37 @@ def test_mla_validation(lib, kw, expect):
 
 def test_mla_empty_is_ok_without_pointers(lib):
     assert mla(lib, q=None, kv=None, m=None, l=None, acc=None, B=0) == OK
+
+
+def mla_fused(lib, q=FAKE, kv=FAKE, m=FAKE, l=FAKE, acc=FAKE, cnt=FAKE, dt=BF16, o=FAKE, lse=None, B=2, H=16,
+              Lk=100, Dqk=576, Dv=512, S=4, scale=0.1):
+    return lib.rf_mla_decode(q, kv, m, l, acc, cnt, dt, o, lse, B, H, Lk, Dqk, Dv, S, scale, None)
+
+
+@pytest.mark.parametrize(
+    "kw,expect",
+    [
+        (dict(S=0), INVALID),
+        (dict(Lk=0), INVALID),
+        (dict(acc=None), INVALID),
+        (dict(kv=MISALIGNED), INVALID),
+        (dict(Dv=256), UNSUPPORTED),
+        (dict(H=8), UNSUPPORTED),
+        (dict(cnt=None), INVALID),
+        (dict(cnt=ctypes.c_void_p(0x10002)), INVALID),
+        (dict(o=None), INVALID),
+        (dict(o=MISALIGNED), INVALID),
+        (dict(lse=ctypes.c_void_p(0x10002)), INVALID),
+        (dict(dt=5), INVALID),
+    ],
+)
+def test_mla_fused_validation(lib, kw, expect):
+    assert mla_fused(lib, **kw) == expect
+    assert lib.rf_last_error().startswith(b"rf_mla_decode")
+
+
+def test_mla_fused_empty_is_ok_without_pointers(lib):
+    assert mla_fused(lib, q=None, kv=None, m=None, l=None, acc=None, cnt=None, o=None, B=0) == OK
 
 
 def test_merge_validation(lib):

@@ -21,9 +21,9 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 DQK, DV = 576, 512
 
 
-def _check(B, H, Lk, S, scale, seed=5, partials=True):
+def _check(B, H, Lk, S, scale, seed=5, partials=True, fused=False):
     q, kv = inputs.mla_inputs(seed, B, H, Lk)
-    o, lse, (m, l, acc) = rf.mla_decode(q.to(DEV), kv.to(DEV), scale, S, out_dtype=torch.float32)
+    o, lse, (m, l, acc) = rf.mla_decode(q.to(DEV), kv.to(DEV), scale, S, out_dtype=torch.float32, fused=fused)
     lat = kv[:, None]                      # [B, 1, Lk, 576]: one shared latent head
     if partials:
         m_ref, l_ref, acc_ref = oracle.decode_partials(q, lat, lat[..., :DV], scale, S)
@@ -58,6 +58,46 @@ def _check(B, H, Lk, S, scale, seed=5, partials=True):
 def test_mla_partials_and_merge_small(B, H, Lk, S):
     print_case(test="mla_small", B=B, H=H, Lk=Lk, S=S)
     _check(B, H, Lk, S, 1 / math.sqrt(DQK))
+
+
+@pytest.mark.parametrize(
+    "B,H,Lk,S",
+    [
+        (1, 16, 1000, 1),     # one workgroup per group: it merges its own state
+        (2, 16, 777, 16),
+        (1, 16, 5, 4),        # an empty segment still counts itself in
+        (1, 16, 100, 64),     # many empty segments
+        (3, 32, 513, 3),      # two head groups per sequence, three sequences
+        (1, 128, 300, 2),
+    ],
+)
+def test_mla_fused_merge(B, H, Lk, S):
+    """rf_mla_decode: split and merge in one launch, against the oracle."""
+    print_case(test="mla_fused", B=B, H=H, Lk=Lk, S=S)
+    _check(B, H, Lk, S, 1 / math.sqrt(DQK), fused=True)
+
+
+def test_mla_fused_counters_return_to_zero():
+    """Two calls in a row on one counters array (bf16 output): the counters are
+    0 after each, and both calls give the same output as the two-launch path
+    merged by rf_merge_states (equal up to the merge order's rounding)."""
+    print_case(test="mla_fused_repeat")
+    B, H, Lk, S = 4, 32, 1200, 8
+    scale = 1 / math.sqrt(DQK)
+    q, kv = (t.to(DEV) for t in inputs.mla_inputs(9, B, H, Lk))
+    pm = torch.empty((B, H, S), device=DEV)
+    pl = torch.empty_like(pm)
+    pa = torch.empty((B, H, S, DV), device=DEV)
+    counters = torch.zeros(B * H // 16, dtype=torch.int32, device=DEV)
+    o_ref, lse_ref, _ = rf.mla_decode(q, kv, scale, S, out_dtype=torch.float32)
+    for _ in range(2):
+        o = torch.full((B, H, DV), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((B, H), float("nan"), device=DEV)
+        rf.rf_mla_decode(q, kv, pm, pl, pa, counters, o, lse, scale)
+        torch.cuda.synchronize()
+        assert int(counters.abs().sum()) == 0
+        assert normwise(np32(o), np32(o_ref)) <= 8e-3          # bf16 output rounding
+        assert np.abs(np32(lse) - np32(lse_ref)).max() <= 1e-5 * max(1, np.abs(np32(lse_ref)).max())
 
 
 def test_mla_large_scores():
