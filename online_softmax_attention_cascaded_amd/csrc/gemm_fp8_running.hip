@@ -8,243 +8,272 @@
 // Early K tiles are therefore quantised with a smaller scale than the row's
 // final one (finer steps, different codes from the final-scale path).
 //
-// Workgroup tile 256 x 256, eight waves of 128 x 64 (two per SIMD: 128
-// accumulator registers each, leaving room for the VALU rescale), with
-// v_mfma_f32_32x32x64_f8f6f4 taking B first (a lane holds one row of C and four
-// consecutive columns per register group). Per K step, the bf16 A tile (256
-// rows x 128 bytes) and the e4m3 B tile (256 rows x 64 bytes) go HBM -> LDS by
-// buffer loads to LDS, one step ahead. Then two lanes share each A row (32
-// values each): abs-max (integer max on the bf16 magnitude bits, combined
-// across the pair by v_permlane32_swap), the new scale, the rescale ratio
-// (published in LDS), the codes (correctly rounded x / s by one Markstein
-// correction of x * RN(1/s), hardware round-to-nearest-even e4m3 convert),
-// written into an LDS code tile in the MFMA operand layout. After a barrier
-// each wave rescales its accumulator rows if any ratio differs from 1 and
-// runs the step's 8 MFMAs.
+// Workgroup tile 128 x 512: every A tile is quantised by N / 512 workgroups
+// (the price of having no pre-pass), half as often as with square 256 tiles.
+// Eight waves of 64 x 128 (two per SIMD, 128 accumulator registers each) on
+// v_mfma_f32_32x32x64_f8f6f4 taking B first (a lane holds one row of C and
+// four consecutive columns per register group).
+//
+// Pipeline, one K tile (step) t per barrier: the MFMAs of step t read the code
+// tile of step t and the B stage, while the same waves quantise step t + 1
+// from registers into the other code tile, so the quantiser's VALU work can
+// run beside the matrix cores. B goes HBM -> LDS by buffer loads straight into
+// LDS, 128 K columns (two steps) per stage, two stages; each lane's share of
+// A (4 lanes per row, 16 values per step) is loaded into registers two steps
+// ahead. The quantiser: abs-max on the bf16 magnitude bits (packed 16-bit
+// max), combined over the row's 4 lanes by DPP; on growth the new scale, the
+// ratio s_old / s_new (published in LDS for the step's MFMA waves) and 1 / s;
+// codes as the correctly rounded x / s (one Markstein correction of
+// x * RN(1/s)) through the hardware round-to-nearest-even e4m3 convert (the
+// code of a zero may carry either sign: it adds 0 to every product).
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
 
 namespace rf {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kABytes = BM * BK * 2;           // bf16 A tile, 32 KB
-constexpr int kBBytes = BN * BK;               // e4m3 B tile, 16 KB
-constexpr int kStageBytes = kABytes + kBBytes;  // 48 KB, two stages
-constexpr int kCodeBytes = BM * BK;            // e4m3 A codes of the step, 16 KB
+constexpr int BM = 128, BN = 512, BK = 64;  // BK: K columns per step of the running scale
+constexpr int LK = 128;                      // K columns per B stage (two steps)
+constexpr int kBStage = BN * LK;             // 64 KB of e4m3 B per stage
+constexpr int kCodes = BM * BK;              // 8 KB of e4m3 A codes per step
+constexpr int kOffCodes = 2 * kBStage;
+constexpr int kOffRatio = kOffCodes + 2 * kCodes;
+constexpr int kOffScale = kOffRatio + 2 * BM * 4;
+constexpr int kSmem = kOffScale + BM * 4;    // 145.5 KB
+constexpr int kGroupM = 8;                   // tile rows per band of the tile order
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// Operand tiles (64-byte rows, 16-byte chunks XOR (row >> 2) & 3): conflict-free
-// for the 16-lane passes of ds_read_b128 (same layout as the final-scale GEMM).
-__device__ __forceinline__ int op_off(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 2) & 3)) << 4);
+// B stage: 128-byte rows, 16-byte chunks XOR (row >> 1) & 7, so the operand
+// reads of 16 consecutive rows (one LDS pass of ds_read_b128) use all 64 banks.
+__device__ __forceinline__ int b_off(int row, int chunk) {
+  return row * LK + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
-// bf16 A tile (128-byte rows, 8 chunks): chunk XOR (row & 7), so one lane per
-// row reading chunk c touches at most two rows per bank group.
-__device__ __forceinline__ int a_off(int row, int chunk) {
-  return row * (2 * BK) + ((chunk ^ (row & 7)) << 4);
+// Code tile: 64-byte rows, chunks XOR (row >> 2) & 3 (the same property).
+__device__ __forceinline__ int c_off(int row, int chunk) {
+  return row * BK + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(512, 2) void gemm_fp8_running_kernel(
+// Tile order: workgroups are dealt to the 8 XCDs round-robin, so workgroup b is
+// renumbered to give each XCD a contiguous run of tile ids, which then walk
+// bands of kGroupM tile rows column by column (at 32 x 8 tiles each XCD gets a
+// block of 8 tile rows x 4 tile columns).
+__device__ __forceinline__ void tile_of(int b, int ntm, int ntn, int& tm, int& tn) {
+  const int T = ntm * ntn;
+  const int t = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+  const int first = (t / (kGroupM * ntn)) * kGroupM;
+  const int rows = min(kGroupM, ntm - first);
+  const int r = t - first * ntn;
+  tm = first + r % rows;
+  tn = r / rows;
+}
+
+__global__ __launch_bounds__(512, 1) void gemm_fp8_running_kernel(
     const uint16_t* __restrict__ a, const uint8_t* __restrict__ bq, const float* __restrict__ sb,
     int M, int N, int K, float* __restrict__ a_scale, uint16_t* __restrict__ c, int vec) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes + kCodeBytes];
-  __shared__ float ratio_s[BM];
-  __shared__ float scale_s[BM];
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  float* const ratio_s = reinterpret_cast<float*>(smem + kOffRatio);
+  float* const scale_s = reinterpret_cast<float*>(smem + kOffScale);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;  // 128-row half, 64-column quarter
-  const int ntn = (N + BN - 1) / BN;
-  const int tm = blockIdx.x / ntn, tn = blockIdx.x % ntn;
+  const int wm = wave >> 2, wn = wave & 3;  // 64-row half, 128-column quarter
+  int tm, tn;
+  tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  char* const codes = smem + 2 * kStageBytes;
 
-  // ---- HBM -> LDS. A: wave w fills rows 32 w .. 32 w + 31, four 1 KB blocks of
-  // 8 rows; lane l writes physical chunk l % 8 of row 8 i + l / 8. B: wave w
-  // fills two 1 KB blocks of 16 rows (physical chunk l % 4 of row 16 i + l / 4).
   const __amdgpu_buffer_rsrc_t ars =
       make_rsrc(a + (size_t)m0 * K, (uint32_t)(min(BM, M - m0) * K * 2));
   const __amdgpu_buffer_rsrc_t brs = make_rsrc(bq + (size_t)n0 * K, (uint32_t)(min(BN, N - n0) * K));
-  // Per-lane parts of the load offsets; the per-block parts are immediates.
-  const int arow0 = 32 * wave + (lane >> 3), brow0 = 32 * wave + (lane >> 2);
-  auto issue = [&](int kt) {
-    char* st = smem + (kt & 1) * kStageBytes;
+
+  // ---- B: wave w fills rows 64 w .. 64 w + 63 of a stage, eight 1 KB blocks
+  // of 8 rows; lane l writes physical chunk l % 8 of row 8 i + l / 8. Rows past
+  // N read as 0 (the row offset is in the per-lane offset, which the buffer
+  // range checks).
+  const int brow = 64 * wave + (lane >> 3);
+  auto issue_b = [&](int g) {
+    char* st = smem + (g & 1) * kBStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = arow0 + 8 * i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void*)(st + (4 * wave + i) * 1024), 16,
-                                               row * K * 2 + 16 * ((lane & 7) ^ (row & 7)),
-                                               kt * BK * 2, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int row = brow + 8 * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void*)(st + (8 * wave + i) * 1024), 16,
+                                               row * K + 16 * ((lane & 7) ^ ((row >> 1) & 7)),
+                                               g * LK, 0, 0);
     }
+  };
+
+  // ---- A: lanes 4 r' .. 4 r' + 3 of wave w share row qr = 16 w + r'; lane
+  // quarter q holds chunks (8 bf16) q and q + 4 of each step, so each load
+  // instruction reads 64 contiguous bytes of 16 rows. Rows past M read as 0.
+  const int qr = tid >> 2, q = lane & 3;
+  const int avoff = qr * K * 2 + 16 * q;
+  auto issue_a = [&](int t, u32x4 (&dst)[2]) {
+    dst[0] = buf_load16(ars, avoff, t * BK * 2);
+    dst[1] = buf_load16(ars, avoff + 64, t * BK * 2);
+  };
+
+  // ---- quantiser state of row qr (identical in its 4 lanes).
+  uint32_t amax_bits = 0;  // running abs-max as bf16 magnitude bits
+  float s_run = 0.f, rcp = 0.f;
+
+  // Step t's codes of row qr from its 16 values (chunks q and q + 4 of the
+  // step), the row's ratio for step t.
+  auto quant = [&](int t, const u32x4& x0, const u32x4& x1) {
+    u16x2 m2 = {0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, x0[e] & 0x7fff7fffu));
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, x1[e] & 0x7fff7fffu));
+    }
+    uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kDppQuadXor1, 0xF, 0xF, true));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kDppQuadXor2, 0xF, 0xF, true));
+    float ratio = 1.f;
+    if (m > amax_bits) {
+      // The accumulator row holds the sum in units of s_run; it moves to s_new.
+      const float s_new = __uint_as_float(m << 16) / 448.f;
+      if (amax_bits != 0) ratio = s_run / s_new;
+      amax_bits = m;
+      s_run = s_new;
+      rcp = 1.f / s_new;
+    }
+    if (q == 0) ratio_s[(t & 1) * BM + qr] = ratio;
+    char* const codes = smem + kOffCodes + (t & 1) * kCodes;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const u32x4 xv = k ? x1 : x0;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[2 * e] = bf16_lo(xv[e]);
+        y[2 * e + 1] = bf16_hi(xv[e]);
+      }
+      if (rcp <= 3.4e38f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float q0 = y[j] * rcp;
+          y[j] = fmaf(fmaf(-s_run, q0, y[j]), rcp, q0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = y[j] / s_run;
+      }
+      uint32_t lo = 0u, hi = 0u;
+      if (s_run > 0.f) {
+        lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
+        hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+        hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
+      }
+      // bf16 chunk q (k = 0) or q + 4 (k = 1) -> code bytes 8 q (+ 32) of the row
+      *reinterpret_cast<u32x2*>(codes + c_off(qr, 2 * k + (q >> 1)) + 8 * (q & 1)) = u32x2{lo, hi};
+    }
+  };
+
+  // ---- MFMA operands. A code fragment i: rows wm*64 + 32 i + li; B fragment
+  // j: rows wn*128 + 32 j + li; each lane takes 32 bytes of the step's 64.
+  const int half = lane >> 5, li = lane & 31;
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  auto rd = [](const char* p) { return *reinterpret_cast<const u32x4*>(p); };
+  auto frag = [](const u32x4& lo, const u32x4& hi) {
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto mfma_step = [&](int t) {
+    const char* const codes = smem + kOffCodes + (t & 1) * kCodes;
+    const char* const st = smem + ((t >> 1) & 1) * kBStage;
+    const int ks = 4 * (t & 1);  // first 16-byte chunk of the step in a B row
+    // move the accumulator rows to this step's scales
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int row = brow0 + 16 * i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void*)(st + kABytes + (2 * wave + i) * 1024),
-                                               16, row * K + 16 * ((lane & 3) ^ ((row >> 2) & 3)),
-                                               kt * BK, 0, 0);
-    }
-  };
-
-  // ---- quantiser state: lanes l and l + 32 of wave w share A row qr of the
-  // tile; lane half qh takes columns 32 qh .. 32 qh + 31 (chunks 4 qh .. 4 qh + 3).
-  const int qr = 32 * wave + (lane & 31), qh = lane >> 5;
-  uint32_t amax_bits = 0;  // running abs-max as bf16 magnitude bits
-  float s_run = 0.f;
-
-  // ---- MFMA operands: fragment f < 4 is B rows wn*128 + 32 f + li, f >= 4 is
-  // A code rows wm*128 + 32 (f - 4) + li; 32 bytes of K each.
-  const int half = lane >> 5, li = lane & 31;
-  // Fragment f, half h: f < 2 is B row wn*64 + 32 f + li in the stage, f >= 2
-  // is A code row wm*128 + 32 (f - 2) + li in the code tile.
-  auto fo = [&](int f, int h) {
-    return (f < 2) ? kABytes + op_off(wn * 64 + 32 * f + li, 2 * half + h)
-                   : 2 * kStageBytes + op_off(wm * 128 + 32 * (f - 2) + li, 2 * half + h);
-  };
-  f32x16 acc[4][2];
+      const float rt = ratio_s[(t & 1) * BM + wm * 64 + 32 * i + li];
+      if (__any(rt != 1.f)) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  const int nk = K / BK;
-  issue(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();  // stage kt visible; every wave is done with the previous codes
-    if (kt + 1 < nk) issue(kt + 1);
-    const char* st = smem + (kt & 1) * kStageBytes;
-
-    // ---- running abs-max, scale and codes of row qr for this K tile: one pass
-    // over the row's 64 values for the abs-max, a second to quantise them (LDS
-    // reads are cheap; keeping all 64 in registers would not fit beside the
-    // accumulators).
-    uint32_t tmax = 0;
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(st + a_off(qr, 4 * qh + ch));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) tmax = max(tmax, max(xv[e] & 0x7fffu, (xv[e] >> 16) & 0x7fffu));
-    }
-    {
-      const auto pr = __builtin_amdgcn_permlane32_swap(tmax, tmax, false, false);
-      tmax = max((uint32_t)pr[0], (uint32_t)pr[1]);  // both lanes of the pair
-    }
-    const uint32_t anew_bits = max(amax_bits, tmax);
-    const float s_new = __uint_as_float(anew_bits << 16) / 448.f;
-    // The accumulator row holds the sum in units of s_run; it moves to s_new.
-    if (qh == 0) ratio_s[qr] = (anew_bits > amax_bits && amax_bits != 0) ? s_run / s_new : 1.f;
-    amax_bits = anew_bits;
-    s_run = s_new;
-    const float rcp = (s_new > 0.f) ? 1.f / s_new : 0.f;
-#pragma unroll 1
-    for (int cc = 2 * qh; cc < 2 * qh + 2; ++cc) {  // 16 values -> one 16-byte chunk of codes
-      uint32_t w[4];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(st + a_off(qr, 2 * cc + hh));
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[2 * e] = bf16_lo(xv[e]);
-          y[2 * e + 1] = bf16_hi(xv[e]);
-        }
-        if (rcp <= 3.4e38f) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float q0 = y[j] * rcp;
-            const float r = fmaf(-s_new, q0, y[j]);
-            y[j] = __builtin_copysignf(fmaf(r, rcp, q0), y[j]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) y[j] = y[j] / s_new;
-        }
-        uint32_t lo = 0u, hi = 0u;
-        if (s_new > 0.f) {
-          lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-          lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
-          hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-          hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
-        }
-        w[2 * hh] = lo;
-        w[2 * hh + 1] = hi;
+        for (int j = 0; j < 4; ++j) acc[i][j] *= rt;
       }
-      *reinterpret_cast<u32x4*>(codes + op_off(qr, cc)) = u32x4{w[0], w[1], w[2], w[3]};
     }
-    lds_barrier();  // codes and ratios visible
+    i32x8 fa[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = wm * 64 + 32 * i + li;
+      fa[i] = frag(rd(codes + c_off(row, 2 * half)), rd(codes + c_off(row, 2 * half + 1)));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + 32 * j + li;
+      const i32x8 fb = frag(rd(st + b_off(row, ks + 2 * half)), rd(st + b_off(row, ks + 2 * half + 1)));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i][j] = mfma_fp8(fb, fa[i], acc[i][j]);
+    }
+  };
 
-    // ---- move the accumulator rows of this wave to the new scales.
-    float rt[4];
-    bool grow = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rt[i] = ratio_s[wm * 128 + 32 * i + li];
-      grow |= rt[i] != 1.f;
-    }
-    if (__any(grow)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] *= rt[i];
-    }
-
-    // ---- 8 MFMAs on the step's codes and B tile: the two B fragments once,
-    // each A fragment just before its two MFMAs.
-    auto frag = [&](const char* base, int f) {
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(base + fo(f, 0));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(base + fo(f, 1));
-      return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    };
-    i32x8 fb[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) fb[j] = frag(st, j);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const i32x8 fa = frag(smem, 2 + i);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_fp8(fb[j], fa, acc[i][j]);
-    }
+  // Issue order: step t issues A(t + 2) (2 loads per lane), then at even t
+  // B stage t / 2 + 1 (8 loads per lane). At the start of step t the B stage
+  // of t must have landed: at even t it was issued at step t - 2, followed
+  // only by A(t + 1); at odd t it has already been waited for. The A
+  // registers are waited for where the quantiser first reads them.
+  const int nt = K / BK, ng = K / LK;  // K is a multiple of 128
+  u32x4 A0[2], A1[2];
+  issue_a(0, A0);
+  issue_b(0);
+  issue_a(1, A1);
+  quant(0, A0[0], A0[1]);
+  for (int t = 0; t < nt; t += 2) {
+    // step t (even)
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    lds_barrier();
+    if (t + 2 < nt) issue_a(t + 2, A0);
+    if ((t >> 1) + 1 < ng) issue_b((t >> 1) + 1);
+    mfma_step(t);
+    quant(t + 1, A1[0], A1[1]);
+    // step t + 1 (odd)
+    lds_barrier();
+    if (t + 3 < nt) issue_a(t + 3, A1);
+    mfma_step(t + 1);
+    if (t + 2 < nt) quant(t + 2, A0[0], A0[1]);
   }
 
   // ---- final scales: s_final of each row (and A's scale output, written once
   // per row by the workgroups of the first column tile).
-  if (qh == 0) {
+  if (q == 0) {
     scale_s[qr] = s_run;
     if (tn == 0 && m0 + qr < M) a_scale[m0 + qr] = s_run;
   }
   lds_barrier();
 
-  // Epilogue: lane holds C row m0 + wm*128 + 32 i + li, columns
-  // n0 + wn*64 + 32 j + 8 g + 4 half + (0..3) in registers 4 g .. 4 g + 3.
+  // Epilogue: lane holds C row m0 + wm*64 + 32 i + li, columns
+  // n0 + wn*128 + 32 j + 8 g + 4 half + (0..3) in registers 4 g .. 4 g + 3.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lrow = wm * 128 + 32 * i + li;
+  for (int i = 0; i < 2; ++i) {
+    const int lrow = wm * 64 + 32 * i + li;
     const int row = m0 + lrow;
     if (row >= M) continue;
     const float si = scale_s[lrow];
     uint16_t* crow = c + (size_t)row * N;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = n0 + wn * 64 + 32 * j + 8 * g + 4 * half;
+      for (int gg = 0; gg < 4; ++gg) {
+        const int col = n0 + wn * 128 + 32 * j + 8 * gg + 4 * half;
         if (vec && col + 3 < N) {
-          const f32x4 t = *reinterpret_cast<const f32x4*>(sb + col);
-          const uint32_t lo = pack_bf16x2(acc[i][j][4 * g] * si * t[0], acc[i][j][4 * g + 1] * si * t[1]);
-          const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2] * si * t[2], acc[i][j][4 * g + 3] * si * t[3]);
+          const f32x4 tt = *reinterpret_cast<const f32x4*>(sb + col);
+          const uint32_t lo = pack_bf16x2(acc[i][j][4 * gg] * si * tt[0], acc[i][j][4 * gg + 1] * si * tt[1]);
+          const uint32_t hi = pack_bf16x2(acc[i][j][4 * gg + 2] * si * tt[2], acc[i][j][4 * gg + 3] * si * tt[3]);
           *reinterpret_cast<u32x2*>(crow + col) = u32x2{lo, hi};
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (col + e < N)
-              crow[col + e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * g + e] * si * sb[col + e]));
+              crow[col + e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * gg + e] * si * sb[col + e]));
         }
       }
     }
