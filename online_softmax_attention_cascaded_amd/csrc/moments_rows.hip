@@ -21,8 +21,8 @@
 // Mappings. Thread and wave level: one wave per row (4 rows per workgroup);
 // lane l holds the 16-byte chunks l + 64 j of its row. Block level: one
 // workgroup per row, thread t holds chunks t + 256 j. The fused forms load the
-// whole row once through buffer loads (chunks past the row read as 0 with no
-// memory traffic and carry no mass). Unfused: one kernel for the centre, a
+// whole row once through buffer loads with the streaming cache policy (chunks
+// past the row read as 0 with no memory traffic and carry no mass). Unfused: one kernel for the centre, a
 // second one for the centred sum, each reading the row.
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
@@ -72,7 +72,7 @@ __device__ __forceinline__ float centred(f32x4 y, f32x4 w, float c) {
 }
 
 __device__ __forceinline__ f32x4 load_chunk(__amdgpu_buffer_rsrc_t r, int chunk) {
-  return __builtin_bit_cast(f32x4, buf_load16(r, chunk * 16, 0));
+  return __builtin_bit_cast(f32x4, buf_load16_stream(r, chunk * 16, 0));
 }
 
 // Positions (shifted) and masses of one chunk; unit masses when !WEIGHTED,

@@ -29,6 +29,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
+// Cache policy for bytes that are read once (non-temporal, streaming). On
+// MI355X it lifts a plain HBM read stream from about 6.2 to 7.0 TB/s. Data
+// that other workgroups read again from L2 (attention K/V tiles, GEMM
+// operands) keeps the default policy: there the hint measured slower.
+constexpr int kStreamPolicy = 2;
+__device__ __forceinline__ u32x4 buf_load16_stream(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamPolicy);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
