@@ -11,21 +11,22 @@
 // Workgroup tile 128 x 512: every A tile is quantised by N / 512 workgroups
 // (the price of having no pre-pass), half as often as with square 256 tiles.
 // Eight waves of 64 x 128 (two per SIMD, 128 accumulator registers each) on
-// v_mfma_f32_32x32x64_f8f6f4 taking B first (a lane holds one row of C and
-// four consecutive columns per register group).
+// v_mfma_f32_32x32x64_f8f6f4 taking A first: a lane holds one column of C and,
+// in each group of four registers, rows 8 g + 0..3 of a 32-row block (+ 4 in
+// the upper half of the wave), so a rescale touches only the register groups
+// whose rows moved.
 //
 // Pipeline, one K tile (step) t per barrier: the MFMAs of step t read the code
 // tile of step t and the B stage, while the same waves quantise step t + 1
-// from registers into the other code tile, so the quantiser's VALU work can
-// run beside the matrix cores. B goes HBM -> LDS by buffer loads straight into
+// from registers into the other code tile, so the quantiser's VALU work and
+// the matrix cores overlap. B goes HBM -> LDS by buffer loads straight into
 // LDS, 128 K columns (two steps) per stage, two stages; each lane's share of
-// A (4 lanes per row, 16 values per step) is loaded into registers two steps
+// A (4 lanes per row, 16 values per step) is loaded into registers a stage
 // ahead. The quantiser: abs-max on the bf16 magnitude bits (packed 16-bit
 // max), combined over the row's 4 lanes by DPP; on growth the new scale, the
 // ratio s_old / s_new (published in LDS for the step's MFMA waves) and 1 / s;
 // codes as the correctly rounded x / s (one Markstein correction of
-// x * RN(1/s)) through the hardware round-to-nearest-even e4m3 convert (the
-// code of a zero may carry either sign: it adds 0 to every product).
+// x * RN(1/s)) through the hardware round-to-nearest-even e4m3 convert.
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
 
@@ -192,13 +193,30 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_running_kernel(
     const char* const codes = smem + kOffCodes + (t & 1) * kCodes;
     const char* const st = smem + ((t >> 1) & 1) * kBStage;
     const int ks = 4 * (t & 1);  // first 16-byte chunk of the step in a B row
-    // move the accumulator rows to this step's scales
+    // Move the accumulator rows whose scale grew to this step's scale. Lane l
+    // reads the ratio of row wm*64 + l; the ballot tells every lane which rows
+    // moved. Register e of block i holds row 8 (e / 4) + e % 4 (lanes 0-31)
+    // or that + 4 (lanes 32-63) of the block, so a group of four registers
+    // covers 8 rows and is multiplied only when one of them moved, each lane by
+    // the ratios of its own rows (exactly 1 for rows that did not move).
+    const float rl = ratio_s[(t & 1) * BM + wm * 64 + lane];
+    const uint64_t moved = __ballot(rl != 1.f);
+    if (moved) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float rt = ratio_s[(t & 1) * BM + wm * 64 + 32 * i + li];
-      if (__any(rt != 1.f)) {
+      for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] *= rt;
+        for (int gq = 0; gq < 4; ++gq) {
+          // registers 4 gq .. 4 gq + 3 of block i: rows 8 gq + 0..3 (+ 4 for
+          // lanes 32-63) of the block; rows that did not move have ratio 1
+          if ((moved >> (32 * i + 8 * gq)) & 0xffull) {
+            const f32x4 rt = *reinterpret_cast<const f32x4*>(
+                ratio_s + (t & 1) * BM + wm * 64 + 32 * i + 8 * gq + 4 * half);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[i][j][4 * gq + k] *= rt[k];
+          }
+        }
       }
     }
     i32x8 fa[2];
@@ -212,7 +230,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_running_kernel(
       const int row = wn * 128 + 32 * j + li;
       const i32x8 fb = frag(rd(st + b_off(row, ks + 2 * half)), rd(st + b_off(row, ks + 2 * half + 1)));
 #pragma unroll
-      for (int i = 0; i < 2; ++i) acc[i][j] = mfma_fp8(fb, fa[i], acc[i][j]);
+      for (int i = 0; i < 2; ++i) acc[i][j] = mfma_fp8(fa[i], fb, acc[i][j]);
     }
   };
 
@@ -250,30 +268,37 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_running_kernel(
   }
   lds_barrier();
 
-  // Epilogue: lane holds C row m0 + wm*64 + 32 i + li, columns
-  // n0 + wn*128 + 32 j + 8 g + 4 half + (0..3) in registers 4 g .. 4 g + 3.
+  // Epilogue: lane holds C column n0 + wn*128 + 32 j + li and, in register e
+  // of block i, row m0 + wm*64 + 32 i + 8 (e / 4) + 4 half + e % 4. Lanes 2p and
+  // 2p + 1 trade one value of each register pair (e, e + 1), so the even lane
+  // stores columns (n, n + 1) of the pair's first row and the odd lane those
+  // of its second row, 4 bytes each.
+  const bool odd = lane & 1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int lrow = wm * 64 + 32 * i + li;
-    const int row = m0 + lrow;
-    if (row >= M) continue;
-    const float si = scale_s[lrow];
-    uint16_t* crow = c + (size_t)row * N;
+  for (int j = 0; j < 4; ++j) {
+    const int col = n0 + wn * 128 + 32 * j + li;
+    const float tj = col < N ? sb[col] : 0.f;
+    const int pcol = col & ~1;  // first column of the lane pair
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int col = n0 + wn * 128 + 32 * j + 8 * gg + 4 * half;
-        if (vec && col + 3 < N) {
-          const f32x4 tt = *reinterpret_cast<const f32x4*>(sb + col);
-          const uint32_t lo = pack_bf16x2(acc[i][j][4 * gg] * si * tt[0], acc[i][j][4 * gg + 1] * si * tt[1]);
-          const uint32_t hi = pack_bf16x2(acc[i][j][4 * gg + 2] * si * tt[2], acc[i][j][4 * gg + 3] * si * tt[3]);
-          *reinterpret_cast<u32x2*>(crow + col) = u32x2{lo, hi};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < N)
-              crow[col + e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * gg + e] * si * sb[col + e]));
+      for (int e = 0; e < 16; e += 2) {
+        const int lrow = wm * 64 + 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
+        const float v0 = acc[i][j][e] * scale_s[lrow] * tj;          // row lrow
+        const float v1 = acc[i][j][e + 1] * scale_s[lrow + 1] * tj;  // row lrow + 1
+        const float send = odd ? v0 : v1;
+        const float got = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(send), kDppQuadXor1, 0xF, 0xF, true));
+        const int row = m0 + lrow + (odd ? 1 : 0);
+        const float lo = odd ? got : v0, hi = odd ? v1 : got;
+        if (row < M) {
+          uint16_t* dst = c + (size_t)row * N + pcol;
+          if (vec && pcol + 1 < N) {
+            *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(lo, hi);
+          } else {
+            if (pcol < N) dst[0] = __builtin_bit_cast(uint16_t, (__bf16)lo);
+            if (pcol + 1 < N) dst[1] = __builtin_bit_cast(uint16_t, (__bf16)hi);
+          }
         }
       }
     }
@@ -285,8 +310,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_running_kernel(
 hipError_t launch_gemm_fp8_running(const void* a, const uint8_t* b_q, const float* b_scale, int M,
                                    int N, int K, float* a_scale, void* c, hipStream_t stream) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int vec = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(c) % 8 == 0) &&
-                  (reinterpret_cast<uintptr_t>(b_scale) % 16 == 0);
+  const int vec = (N % 2 == 0) && (reinterpret_cast<uintptr_t>(c) % 4 == 0);
   hipLaunchKernelGGL(gemm_fp8_running_kernel, dim3(tiles), dim3(512), 0, stream,
                      static_cast<const uint16_t*>(a), b_q, b_scale, M, N, K, a_scale,
                      static_cast<uint16_t*>(c), vec);
