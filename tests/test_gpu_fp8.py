@@ -126,7 +126,7 @@ def _running_case(a, bsrc):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 64, 256), (300, 200, 512), (256, 512, 1024), (1, 3, 128),
-                                   (513, 260, 7168)])
+                                   (513, 260, 7168), (129, 517, 256)])
 def test_running_scale_gemm_small(M, N, K):
     print_case(test="gemm_running", M=M, N=N, K=K)
     a, bsrc = inputs.quant_inputs(12, M, N, K)
