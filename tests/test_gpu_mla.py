@@ -53,6 +53,7 @@ def _check(B, H, Lk, S, scale, seed=5, partials=True, fused=False):
         (1, 16, 31, 1),       # fewer keys than a step
         (1, 16, 32, 1),
         (1, 16, 33, 2),
+        (20, 16, 777, 16),    # 320 workgroups, more than the CUs: two-stage ring
     ],
 )
 def test_mla_partials_and_merge_small(B, H, Lk, S):
@@ -69,6 +70,7 @@ def test_mla_partials_and_merge_small(B, H, Lk, S):
         (1, 16, 100, 64),     # many empty segments
         (3, 32, 513, 3),      # two head groups per sequence, three sequences
         (1, 128, 300, 2),
+        (20, 16, 777, 16),    # two-stage ring (more workgroups than CUs)
     ],
 )
 def test_mla_fused_merge(B, H, Lk, S):
