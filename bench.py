@@ -42,6 +42,13 @@ FP8 = dict(M=4096, N=4096, K=7168)
 MLA = dict(B=32, H=16, Lk=8192, dqk=576, dv=512)
 MLA_SEGMENTS = (8, 16, 32)
 SOFTMAX_VALUES = 1 << 26
+ROW_ROTATE = 3  # input copies per row length, so no launch re-reads the last one from cache
+
+
+def rotated(t, n=ROW_ROTATE):
+    """n device copies of t with rows rolled by 0, 7, 14, ...: the same rows at
+    other addresses (row results are unchanged, only their order)."""
+    return [t] + [t.roll(7 * r, dims=0).contiguous() for r in range(1, n)]
 SOFTMAX_E = (1024, 2048, 4096, 8192)
 DECODE_SEGMENTS = (4, 8, 16, 64)
 ROUTING_ROTATE = 20
@@ -419,7 +426,8 @@ def main():
     progress("multi-latent decode timed")
 
     # Safe softmax alone at each fusion level of the reduction tree, rows of
-    # 1K .. 8K fp32 values, 2^26 values per launch. The rate is counted with the
+    # 1K .. 8K fp32 values, 2^26 values per launch (launches rotate over three
+    # copies of the input, 268 MB each). The rate is counted with the
     # fused form's algorithmic bytes (x read once, y written once: 8 B/value)
     # for every level, so the rates compare like for like; the unfused cascade
     # moves 16 B/value (three reads of x, one write).
@@ -428,15 +436,15 @@ def main():
     sm_rates = {}
     for E in SOFTMAX_E:
         T = SOFTMAX_VALUES // E
-        xs = inputs.softmax_inputs(6, T, E).to(dev)
-        ys = torch.empty_like(xs)
+        xs = rotated(inputs.softmax_inputs(6, T, E).to(dev))
+        ys = torch.empty_like(xs[0])
         work = torch.empty(2 * T, device=dev)
         for lname, lv in levels.items():
-            for _ in range(10):
-                rf.rf_softmax(xs, lv, work, ys)
+            for i in range(10):
+                rf.rf_softmax(xs[i % ROW_ROTATE], lv, work, ys)
             e0.record()
-            for _ in range(args.steps):
-                rf.rf_softmax(xs, lv, work, ys)
+            for i in range(args.steps):
+                rf.rf_softmax(xs[i % ROW_ROTATE], lv, work, ys)
             e1.record()
             torch.cuda.synchronize()
             t_sm = e0.elapsed_time(e1) / 1e3 / args.steps
@@ -456,32 +464,36 @@ def main():
     progress("softmax fusion levels timed")
 
     # Variance and moment of inertia (centre, then centred second moment) at
-    # each fusion level, rows of 1K .. 8K values, 2^26 values per launch.
+    # each fusion level, rows of 1K .. 8K values, 2^26 values per launch
+    # (rotating over three copies of the input).
     # Algorithmic bytes: 4 B/value (x) for the variance, 8 B/value (x and the
     # masses) for the moment of inertia; the unfused cascade reads them twice.
     mom = {}
     for E in SOFTMAX_E:
         T = SOFTMAX_VALUES // E
-        xm, wm = (t.to(dev) for t in inputs.moment_inputs(8, T, E))
+        xm0, wm0 = (t.to(dev) for t in inputs.moment_inputs(8, T, E))
+        sets = list(zip(rotated(xm0), rotated(wm0)))
+        del xm0, wm0
         oc = torch.empty(T, device=dev)
         oi = torch.empty(T, device=dev)
         for kind, per_value in (("variance", 4), ("inertia", 8)):
             for lname, lv in levels.items():
-                def call():
+                def call(i):
+                    xm, wm = sets[i % ROW_ROTATE]
                     if kind == "variance":
                         rf.rf_row_variance(xm, lv, oc, oi)
                     else:
                         rf.rf_row_inertia(xm, wm, lv, oc, oi)
-                for _ in range(10):
-                    call()
+                for i in range(10):
+                    call(i)
                 e0.record()
-                for _ in range(args.steps):
-                    call()
+                for i in range(args.steps):
+                    call(i)
                 e1.record()
                 torch.cuda.synchronize()
                 t_m = e0.elapsed_time(e1) / 1e3 / args.steps
                 mom[(kind, E, lname)] = (t_m, per_value * T * E / t_m / 1e9)
-        del xm, wm, oc, oi
+        del sets, oc, oi
     result["moment_fusion_levels"] = {
         kind: {
             "unit": f"GB/s at {per_value} B/value",
@@ -649,12 +661,12 @@ def main():
     sm_v, var_v = {}, {}
     for E in SOFTMAX_E:
         T = SOFTMAX_VALUES // E
-        xs = inputs.softmax_inputs(6, T, E).to(dev)
-        t_v = vendor_time(lambda i: torch.softmax(xs, dim=-1), 10)
+        xs = rotated(inputs.softmax_inputs(6, T, E).to(dev))
+        t_v = vendor_time(lambda i: torch.softmax(xs[i % ROW_ROTATE], dim=-1), 10)
         sm_v[f"E{E}"] = {"GBs": round(8.0 * T * E / t_v / 1e9, 1),
                          "speedup": round(t_v / sm_rates[(E, "block")][0], 3)}
-        xm, _ = (t.to(dev) for t in inputs.moment_inputs(8, T, E))
-        t_v = vendor_time(lambda i: torch.var_mean(xm, dim=-1, unbiased=False), 10)
+        xm = rotated(inputs.moment_inputs(8, T, E)[0].to(dev))
+        t_v = vendor_time(lambda i: torch.var_mean(xm[i % ROW_ROTATE], dim=-1, unbiased=False), 10)
         best = min(mom[("variance", E, ln)][0] for ln in levels if ln != "unfused")
         var_v[f"E{E}"] = {"GBs": round(4.0 * T * E / t_v / 1e9, 1), "speedup": round(t_v / best, 3)}
         del xs, xm
