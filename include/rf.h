@@ -31,8 +31,12 @@
  *   - Outputs must not alias inputs.
  *   - Calls only enqueue work on `stream` (0 = the null stream) and return.
  *     All arguments are validated before anything is enqueued, so a call that
- *     returns an error has launched nothing; kernel faults surface at the
- *     caller's next synchronisation, as with any HIP launch.
+ *     returns RF_ERR_INVALID_ARG or RF_ERR_UNSUPPORTED has launched nothing.
+ *     RF_ERR_LAUNCH means the HIP runtime refused a launch; the calls that
+ *     enqueue more than one kernel (rf_absmax_quant_gemm_fp8: quantiser,
+ *     then GEMM; rf_softmax level 0: three row passes) stop at the refused
+ *     one, and the kernels enqueued before it stay enqueued. Kernel faults
+ *     surface at the caller's next synchronisation, as with any HIP launch.
  *   - A call whose output is empty (a zero batch or row count) returns RF_OK
  *     and enqueues nothing; null pointers are accepted only then.
  *   - Calls are re-entrant; rf_last_error() is per host thread.
@@ -64,9 +68,9 @@ typedef enum { RF_F32 = 0, RF_BF16 = 1 } rf_dtype;
  * K/V tiles with running (m, l, acc) per query row (transcript cues 15-19).
  *
  *   dt     RF_BF16: q, k, v, o are bf16, math in fp32 (MFMA for both
- *          contractions), d == 128 and one head's K (or V) under 2 GiB
- *          (Lk * d * 2 < 2^31, else RF_ERR_UNSUPPORTED); RF_F32: all fp32
- *          (FMA), d in {64, 128}.
+ *          contractions), d in {64, 128} and one head's K (or V) under
+ *          2 GiB (Lk * d * 2 < 2^31, else RF_ERR_UNSUPPORTED); RF_F32: all
+ *          fp32 (FMA), d in {64, 128}.
  *   q      [B, Hq, Lq, d]      k, v  [B, Hkv, Lk, d]     o  [B, Hq, Lq, d] (dt)
  *   lse    [B, Hq, Lq] fp32 or NULL: m + ln(l) of the scaled scores.
  *   Hq % Hkv == 0; query head h reads key/value head h / (Hq / Hkv).
@@ -87,9 +91,12 @@ rf_status rf_attn_fwd(rf_dtype dt, const void* q, const void* k, const void* v, 
  *   part_acc [B, Hq, S, d]  sum of exp(score - part_m) * v      (0 if empty)
  * all fp32 (transcript cue 39: Multi-Segment; cue 21: the states merge).
  *
- *   dt must be RF_BF16: q [B, Hq, d], k, v [B, Hkv, Lk, d] bf16; d == 128;
- *   Hq % Hkv == 0 and Hq / Hkv <= 16; S >= 1; Lk >= 1; one head's K (or V)
- *   under 2 GiB (Lk * d * 2 < 2^31, else RF_ERR_UNSUPPORTED).
+ *   dt     RF_BF16: q [B, Hq, d], k, v [B, Hkv, Lk, d] bf16, scores and
+ *          P V on MFMA with fp32 accumulation; RF_F32: q, k, v fp32, all
+ *          arithmetic fp32 (FMA).
+ *   d in {64, 128}; Hq % Hkv == 0 and Hq / Hkv <= 16; S >= 1; Lk >= 1; one
+ *   head's K (or V) under 2 GiB (Lk * d * sizeof(element) < 2^31, else
+ *   RF_ERR_UNSUPPORTED).
  */
 rf_status rf_attn_decode_split(rf_dtype dt, const void* q, const void* k, const void* v,
                                float* part_m, float* part_l, float* part_acc, int B, int Hq,

@@ -108,34 +108,87 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+_F32, _BF16, _U8, _I32 = torch.float32, torch.bfloat16, torch.uint8, torch.int32
+
+
+def _expect(fn, name, t, shape, dtypes, optional=False):
+    """The C ABI takes raw pointers and sizes: every buffer's shape and dtype
+    must match the sizes passed beside it, or the kernels would read or write
+    past it. Raises ValueError before anything is launched."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{fn}: {name} is required")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{fn}: {name} has dtype {t.dtype}, expected "
+                         + " or ".join(str(d) for d in dtypes))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _ndim(fn, name, t, n):
+    if t.dim() != n:
+        raise ValueError(f"{fn}: {name} must have {n} dimensions, has shape {tuple(t.shape)}")
+
+
 # ---------------------------------------------------------------- C-named calls
 
 
 def rf_attn_fwd(q, k, v, o, lse, scale, causal):
-    _dev(q, k, v, o, lse)
+    fn = "rf_attn_fwd"
+    _ndim(fn, "q", q, 4)
+    _ndim(fn, "k", k, 4)
     B, Hq, Lq, d = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
+    _expect(fn, "q", q, (B, Hq, Lq, d), (_F32, _BF16))
+    _expect(fn, "k", k, (B, Hkv, Lk, d), q.dtype)
+    _expect(fn, "v", v, (B, Hkv, Lk, d), q.dtype)
+    _expect(fn, "o", o, (B, Hq, Lq, d), q.dtype)
+    _expect(fn, "lse", lse, (B, Hq, Lq), _F32, optional=True)
+    _dev(q, k, v, o, lse)
     _check(lib().rf_attn_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                              B, Hq, Hkv, Lq, Lk, d, float(scale), int(bool(causal)), _stream(q)))
 
 
 def rf_attn_decode_split(q, k, v, part_m, part_l, part_acc, scale):
+    fn = "rf_attn_decode_split"
+    _ndim(fn, "k", k, 4)
+    _ndim(fn, "part_m", part_m, 3)
+    B, Hkv, Lk, d = k.shape
+    Hq, S = part_m.shape[1], part_m.shape[2]
+    _expect(fn, "k", k, (B, Hkv, Lk, d), (_F32, _BF16))
+    _expect(fn, "q", q, (B, Hq, d), k.dtype)
+    _expect(fn, "v", v, (B, Hkv, Lk, d), k.dtype)
+    _expect(fn, "part_m", part_m, (B, Hq, S), _F32)
+    _expect(fn, "part_l", part_l, (B, Hq, S), _F32)
+    _expect(fn, "part_acc", part_acc, (B, Hq, S, d), _F32)
     _dev(q, k, v, part_m, part_l, part_acc)
-    B, Hq, d = q.shape
-    Hkv, Lk = k.shape[1], k.shape[2]
-    S = part_m.shape[-1]
     _check(lib().rf_attn_decode_split(_dtype_code(k), _ptr(q), _ptr(k), _ptr(v), _ptr(part_m),
                                       _ptr(part_l), _ptr(part_acc), B, Hq, Hkv, Lk, d, S,
-                                      float(scale), _stream(q)))
+                                      float(scale), _stream(k)))
 
 
-def rf_mla_decode_split(q, kv, part_m, part_l, part_acc, scale):
-    _dev(q, kv, part_m, part_l, part_acc)
-    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
-        raise ValueError("rf_mla_decode_split takes bf16 q and latent rows")
+def _mla_shapes(fn, q, kv, part_m, part_l, part_acc):
+    _ndim(fn, "q", q, 3)
+    _ndim(fn, "kv", kv, 3)
+    _ndim(fn, "part_acc", part_acc, 4)
     B, H, Dqk = q.shape
     Lk = kv.shape[1]
     S, Dv = part_acc.shape[2], part_acc.shape[3]
+    _expect(fn, "q", q, (B, H, Dqk), _BF16)
+    _expect(fn, "kv", kv, (B, Lk, Dqk), _BF16)
+    _expect(fn, "part_m", part_m, (B, H, S), _F32)
+    _expect(fn, "part_l", part_l, (B, H, S), _F32)
+    _expect(fn, "part_acc", part_acc, (B, H, S, Dv), _F32)
+    return B, H, Dqk, Lk, S, Dv
+
+
+def rf_mla_decode_split(q, kv, part_m, part_l, part_acc, scale):
+    fn = "rf_mla_decode_split"
+    B, H, Dqk, Lk, S, Dv = _mla_shapes(fn, q, kv, part_m, part_l, part_acc)
+    _dev(q, kv, part_m, part_l, part_acc)
     _check(lib().rf_mla_decode_split(_ptr(q), _ptr(kv), _ptr(part_m), _ptr(part_l), _ptr(part_acc),
                                      B, H, Lk, Dqk, Dv, S, float(scale), _stream(q)))
 
@@ -143,76 +196,119 @@ def rf_mla_decode_split(q, kv, part_m, part_l, part_acc, scale):
 def rf_mla_decode(q, kv, part_m, part_l, part_acc, counters, o, lse, scale):
     """Split and merge in one launch; counters int32 [B * H / 16], zero on entry
     and left zero."""
+    fn = "rf_mla_decode"
+    B, H, Dqk, Lk, S, Dv = _mla_shapes(fn, q, kv, part_m, part_l, part_acc)
+    _expect(fn, "counters", counters, (B * H // 16,), _I32)
+    _expect(fn, "o", o, (B, H, Dv), (_F32, _BF16))
+    _expect(fn, "lse", lse, (B, H), _F32, optional=True)
     _dev(q, kv, part_m, part_l, part_acc, counters, o, lse)
-    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
-        raise ValueError("rf_mla_decode takes bf16 q and latent rows")
-    if counters.dtype != torch.int32:
-        raise ValueError("counters must be int32")
-    B, H, Dqk = q.shape
-    Lk = kv.shape[1]
-    S, Dv = part_acc.shape[2], part_acc.shape[3]
     _check(lib().rf_mla_decode(_ptr(q), _ptr(kv), _ptr(part_m), _ptr(part_l), _ptr(part_acc), _ptr(counters),
                                _dtype_code(o), _ptr(o), _ptr(lse), B, H, Lk, Dqk, Dv, S, float(scale), _stream(q)))
 
 
 def rf_merge_states(part_m, part_l, part_acc, o, lse):
+    fn = "rf_merge_states"
+    if part_acc.dim() < 2:
+        raise ValueError(f"{fn}: part_acc must be [..., S, d], has shape {tuple(part_acc.shape)}")
+    lead, (S, d) = tuple(part_acc.shape[:-2]), tuple(part_acc.shape[-2:])
+    rows = 1
+    for x in lead:
+        rows *= x
+    _expect(fn, "part_acc", part_acc, lead + (S, d), _F32)
+    _expect(fn, "part_m", part_m, lead + (S,), _F32)
+    _expect(fn, "part_l", part_l, lead + (S,), _F32)
+    _expect(fn, "o", o, lead + (d,), (_F32, _BF16))
+    _expect(fn, "lse", lse, lead, _F32, optional=True)
     _dev(part_m, part_l, part_acc, o, lse)
-    S, d = part_acc.shape[-2], part_acc.shape[-1]
-    rows = part_m.numel() // S if S else 0
     _check(lib().rf_merge_states(_ptr(part_m), _ptr(part_l), _ptr(part_acc), rows, S, d,
                                  _dtype_code(o), _ptr(o), _ptr(lse), _stream(part_m)))
 
 
 def rf_softmax_topk(logits, k, renormalize, weights, indices):
-    _dev(logits, weights, indices)
+    fn = "rf_softmax_topk"
+    _ndim(fn, "logits", logits, 2)
     T, E = logits.shape
-    _check(lib().rf_softmax_topk(_ptr(logits), T, E, int(k), int(bool(renormalize)), _ptr(weights),
+    k = int(k)
+    _expect(fn, "logits", logits, (T, E), _F32)
+    _expect(fn, "weights", weights, (T, k), _F32)
+    _expect(fn, "indices", indices, (T, k), _I32)
+    _dev(logits, weights, indices)
+    _check(lib().rf_softmax_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(weights),
                                  _ptr(indices), _stream(logits)))
 
 
 def rf_softmax(x, level, work, y):
-    _dev(x, work, y)
-    if x.dtype != torch.float32 or y.dtype != torch.float32:
-        raise ValueError("rf_softmax takes fp32 x and y")
+    fn = "rf_softmax"
+    _ndim(fn, "x", x, 2)
     T, E = x.shape
+    _expect(fn, "x", x, (T, E), _F32)
+    _expect(fn, "y", y, (T, E), _F32)
+    _expect(fn, "work", work, (2 * T,), _F32, optional=True)
+    _dev(x, work, y)
     _check(lib().rf_softmax(_ptr(x), T, E, int(level), _ptr(work), _ptr(y), _stream(x)))
 
 
 def rf_row_variance(x, level, mean, var):
-    _dev(x, mean, var)
-    if x.dtype != torch.float32:
-        raise ValueError("rf_row_variance takes fp32 x")
+    fn = "rf_row_variance"
+    _ndim(fn, "x", x, 2)
     T, E = x.shape
+    _expect(fn, "x", x, (T, E), _F32)
+    _expect(fn, "mean", mean, (T,), _F32)
+    _expect(fn, "var", var, (T,), _F32)
+    _dev(x, mean, var)
     _check(lib().rf_row_variance(_ptr(x), T, E, int(level), _ptr(mean), _ptr(var), _stream(x)))
 
 
 def rf_row_inertia(x, w, level, centre, inertia):
-    _dev(x, w, centre, inertia)
-    if x.dtype != torch.float32 or w.dtype != torch.float32 or w.shape != x.shape:
-        raise ValueError("rf_row_inertia takes fp32 x and w of one shape")
+    fn = "rf_row_inertia"
+    _ndim(fn, "x", x, 2)
     T, E = x.shape
+    _expect(fn, "x", x, (T, E), _F32)
+    _expect(fn, "w", w, (T, E), _F32)
+    _expect(fn, "centre", centre, (T,), _F32)
+    _expect(fn, "inertia", inertia, (T,), _F32)
+    _dev(x, w, centre, inertia)
     _check(lib().rf_row_inertia(_ptr(x), _ptr(w), T, E, int(level), _ptr(centre), _ptr(inertia),
                                 _stream(x)))
 
 
 def rf_absmax_quant_fp8(x, q, scale):
-    _dev(x, q, scale)
+    fn = "rf_absmax_quant_fp8"
+    _ndim(fn, "x", x, 2)
     rows, cols = x.shape
+    _expect(fn, "x", x, (rows, cols), _BF16)
+    _expect(fn, "q", q, (rows, cols), _U8)
+    _expect(fn, "scale", scale, (rows,), _F32)
+    _dev(x, q, scale)
     _check(lib().rf_absmax_quant_fp8(_ptr(x), rows, cols, _ptr(q), _ptr(scale), _stream(x)))
 
 
-def rf_absmax_quant_gemm_fp8(a, b_q, b_scale, a_q, a_scale, c):
-    _dev(a, b_q, b_scale, a_q, a_scale, c)
+def _gemm_shapes(fn, a, b_q, b_scale, a_scale, c):
+    _ndim(fn, "a", a, 2)
+    _ndim(fn, "b_q", b_q, 2)
     M, K = a.shape
     N = b_q.shape[0]
+    _expect(fn, "a", a, (M, K), _BF16)
+    _expect(fn, "b_q", b_q, (N, K), _U8)
+    _expect(fn, "b_scale", b_scale, (N,), _F32)
+    _expect(fn, "a_scale", a_scale, (M,), _F32)
+    _expect(fn, "c", c, (M, N), _BF16)
+    return M, N, K
+
+
+def rf_absmax_quant_gemm_fp8(a, b_q, b_scale, a_q, a_scale, c):
+    fn = "rf_absmax_quant_gemm_fp8"
+    M, N, K = _gemm_shapes(fn, a, b_q, b_scale, a_scale, c)
+    _expect(fn, "a_q", a_q, (M, K), _U8)
+    _dev(a, b_q, b_scale, a_q, a_scale, c)
     _check(lib().rf_absmax_quant_gemm_fp8(_ptr(a), _ptr(b_q), _ptr(b_scale), M, N, K, _ptr(a_q),
                                           _ptr(a_scale), _ptr(c), _stream(a)))
 
 
 def rf_absmax_quant_gemm_fp8_running(a, b_q, b_scale, a_scale, c):
+    fn = "rf_absmax_quant_gemm_fp8_running"
+    M, N, K = _gemm_shapes(fn, a, b_q, b_scale, a_scale, c)
     _dev(a, b_q, b_scale, a_scale, c)
-    M, K = a.shape
-    N = b_q.shape[0]
     _check(lib().rf_absmax_quant_gemm_fp8_running(_ptr(a), _ptr(b_q), _ptr(b_scale), M, N, K,
                                                   _ptr(a_scale), _ptr(c), _stream(a)))
 

@@ -1,4 +1,4 @@
-// bf16 attention forward for head size 128 on gfx950 MFMA.
+// bf16 attention forward for head sizes 64 and 128 on gfx950 MFMA.
 //
 // One pass over 64-key tiles of K and V per block of 128 query rows, with a
 // running reference max m, running denominator l and an fp32 accumulator per
@@ -35,10 +35,9 @@
 namespace rf {
 namespace {
 
-constexpr int D = 128;
 constexpr int BM = 128;                 // query rows per workgroup, 32 per wave
 constexpr int BN = 64;                  // keys per tile
-constexpr int kTileBytes = BN * D * 2;  // 16 KB per operand tile
+constexpr int kMaxTileBytes = BN * 128 * 2;  // 16 KB per operand tile at head size 128
 constexpr float kTau = 8.f;             // lazy-rescale threshold, exp2 units
 constexpr float kPmax = 256.f;          // 2^kTau: largest probability against the reference
 constexpr int KA = 3;                   // K fragment reads run this many MFMAs ahead
@@ -58,13 +57,39 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
-template <bool CAUSAL>
+// Geometry of one head size: rows of K and V are 2 D bytes, D / 8 chunks of
+// 16 bytes. K's swizzle spreads the 16 consecutive rows that one operand read
+// touches over all 256 bytes of the bank space; V's is even, so each 32-byte
+// pair of chunks stays together for the transposing reads, and rows 8 and 16
+// apart share it.
+template <int D>
+struct Geo {
+  static constexpr int kRow = 2 * D;
+  static constexpr int kTileBytes = BN * kRow;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kRowsPerKB = 1024 / kRow;
+  static constexpr int kLoads = kTileBytes / 1024 / 4;  // 1 KB loads per wave per tile
+  static constexpr int ND = D / 16;                     // k-steps of the score product
+  static constexpr int NDB = D / 32;                    // 32-column blocks of the output
+  static constexpr int NSM = 2 * ND;                    // score MFMAs per tile
+  static constexpr int NPV = 4 * NDB;                   // P V MFMAs per tile
+  static __device__ __forceinline__ int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  static __device__ __forceinline__ int vswz(int row) { return D == 128 ? 2 * (row & 7) : 2 * (row & 3); }
+};
+
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int BH,
     int Hq, int Hkv, int Lq, int Lk, float c, int nqb) {
-  // [K0 | K1 | V0 | V1], 16 KB each.
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
+  using Gm = Geo<D>;
+  constexpr int kRow = Gm::kRow, kTileBytes = Gm::kTileBytes, ND = Gm::ND, NDB = Gm::NDB;
+  constexpr int NSM = Gm::NSM, NPV = Gm::NPV;
+  // [K0 | K1 | V0 | V1], one tile each, sized for head size 128 (a size that
+  // depends on the template argument keeps the host pass from emitting the
+  // kernel). Arrays the lambdas below capture are sized for head size 128 for
+  // the same reason; head size 64 uses their leading elements.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kMaxTileBytes];
 
   // Workgroup -> (batch*head, work unit). A unit is one query block, or for
   // causal attention the pair of blocks u and nqb-1-u, so every unit has the
@@ -101,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   // Q^T as the B operand of S^T = K Q^T: lane holds q row `li`, d = 16*ds + 8*g + [0, 8).
   bf16x8 qf[8];
 #pragma unroll
-  for (int ds = 0; ds < 8; ++ds) {
+  for (int ds = 0; ds < ND; ++ds) {
     u32x4 w = {0u, 0u, 0u, 0u};
     if (qrow < Lq) w = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * D + 16 * ds + 8 * g);
     qf[ds] = __builtin_bit_cast(bf16x8, w);
@@ -110,38 +135,39 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
   const int ntiles = (kend + BN - 1) / BN;
 
-  // ---- HBM -> LDS. Each wave fills four 1 KB blocks (4 rows of 256 B) per
-  // tile; lane l writes 16 bytes at block + 16 l, i.e. row 16*wave + 4*i + l/16,
-  // physical chunk l%16, so it fetches the logical chunk that the swizzle puts
-  // there: K chunk = phys ^ (row & 15), V chunk = phys ^ 2*(row & 7).
-  const uint32_t kv_bytes = (uint32_t)Lk * D * 2;
+  // ---- HBM -> LDS. Each wave fills kLoads 1 KB blocks per tile; lane l writes
+  // 16 bytes at block + 16 l, i.e. row blk * kRowsPerKB + l / kChunks, physical
+  // chunk l % kChunks, so it fetches the logical chunk that the swizzle puts
+  // there.
+  const uint32_t kv_bytes = (uint32_t)Lk * kRow;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, kv_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, kv_bytes);
   int kso[4], vso[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * wave + 4 * i + (lane >> 4), pc = lane & 15;
-    kso[i] = row * 256 + ((pc ^ (row & 15)) << 4);
-    vso[i] = row * 256 + ((pc ^ (2 * (row & 7))) << 4);
+  for (int i = 0; i < Gm::kLoads; ++i) {
+    const int row = (Gm::kLoads * wave + i) * Gm::kRowsPerKB + lane / Gm::kChunks;
+    const int pc = lane % Gm::kChunks;
+    kso[i] = row * kRow + ((pc ^ Gm::kswz(row)) << 4);
+    vso[i] = row * kRow + ((pc ^ Gm::vswz(row)) << 4);
   }
   auto load_k = [&](int t, char* buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + (4 * wave + i) * 1024), 16,
-                                               kso[i], t * kTileBytes, 0, 0);
+    for (int i = 0; i < Gm::kLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + (Gm::kLoads * wave + i) * 1024),
+                                               16, kso[i], t * kTileBytes, 0, 0);
   };
   auto load_v = [&](int t, char* buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(buf + (4 * wave + i) * 1024), 16,
-                                               vso[i], t * kTileBytes, 0, 0);
+    for (int i = 0; i < Gm::kLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(buf + (Gm::kLoads * wave + i) * 1024),
+                                               16, vso[i], t * kTileBytes, 0, 0);
   };
 
   // ---- LDS -> registers.
   // K (A operand of S^T): row li (+32 kb), logical chunk 2 ds + g.
   int kr[8];
 #pragma unroll
-  for (int ds = 0; ds < 8; ++ds) kr[ds] = li * 256 + (((2 * ds + g) ^ (li & 15)) << 4);
+  for (int ds = 0; ds < ND; ++ds) kr[ds] = li * kRow + (((2 * ds + g) ^ Gm::kswz(li)) << 4);
   // V^T (A operand of O^T, lane = head-size column 32 db + li, k-slots 8 g..8 g+7).
   // The MFMA k-slots of k-step ks are, for lane half g, the keys
   // 16 ks + 4 g + {0..3} (slots 0..3) and 16 ks + 8 + 4 g + {0..3} (slots 4..7):
@@ -152,15 +178,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   {
     const int j = lane & 15, G = (lane >> 4) & 1;
     const int row = 4 * g + (j >> 2);       // + 16 ks + 8 hh (immediates)
-    const int x = 2 * (row & 7);            // swizzle of every row this lane reads
+    const int x = Gm::vswz(row);            // swizzle of every row this lane reads
     const int cl = 2 * G + ((j >> 1) & 1);  // chunk within the 32-column block
 #pragma unroll
-    for (int db = 0; db < 4; ++db) vr[db] = row * 256 + (((4 * db + cl) ^ x) << 4) + 8 * (j & 1);
+    for (int db = 0; db < NDB; ++db) vr[db] = row * kRow + (((4 * db + cl) ^ x) << 4) + 8 * (j & 1);
   }
 
   f32x16 oacc[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_c = kNegInf;  // reference max of row qrow, in exp2 units (score * c)
   float l_run = 0.f;    // running denominator relative to m_c
 
@@ -170,14 +196,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   char* const V1 = smem + 3 * kTileBytes;
   auto active = [&](int t) { return !CAUSAL || t * BN <= wave_last_row; };
 
-  // Scores of one tile: 8 k-steps on two independent accumulators.
+  // Scores of one tile: ND k-steps on two independent accumulators.
   auto scores = [&](const char* kb, Scores& s) {
     s.s0 = f32x16{};
     s.s1 = f32x16{};
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) {
+    for (int ds = 0; ds < ND; ++ds) {
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + kr[ds]);
-      const bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(kb + kr[ds] + 32 * 256);
+      const bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(kb + kr[ds] + 32 * kRow);
       s.s0 = mfma_bf16(ka, qf[ds], s.s0);
       s.s1 = mfma_bf16(kb1, qf[ds], s.s1);
     }
@@ -218,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       }
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
       return true;
     };
     // Tile 0 sets the reference (every row sees key 0, so it is finite). Later
@@ -229,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     // reference moved if needed and the probabilities recomputed (rare after
     // the first tiles).
     if (t == 0) m_c = row_max_c();
-    // ---- one basic block: the 16 score MFMAs of tile t+1, each K fragment read
+    // ---- one basic block: the NSM score MFMAs of tile t+1, each K fragment read
     // KA MFMAs ahead (the fences keep every read next to its MFMA), and the
     // probabilities of tile t (2 fma, 2 exp2, 1 bf16 pack, 2 adds per pair). The
     // compiler issues the exponentials after the score MFMAs; they overlap with
@@ -240,19 +266,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     nxt.s1 = f32x16{};
     bf16x8 kf[KA + 1];
     auto kread = [&](int i) {
-      return *reinterpret_cast<const bf16x8*>(knext + kr[i >> 1] + (i & 1) * 32 * 256);
+      return *reinterpret_cast<const bf16x8*>(knext + kr[i >> 1] + (i & 1) * 32 * kRow);
     };
 #pragma unroll
     for (int i = 0; i < KA; ++i) kf[i] = kread(i);
     u32x4 pw[4];
     float rs = 0.f;
+    constexpr int EV = 16 / NSM;  // probability pairs per score MFMA
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i + KA < 16) kf[(i + KA) % (KA + 1)] = kread(i + KA);
-      if (i & 1)
-        nxt.s1 = mfma_bf16(kf[i % (KA + 1)], qf[i >> 1], nxt.s1);
-      else
-        nxt.s0 = mfma_bf16(kf[i % (KA + 1)], qf[i >> 1], nxt.s0);
+      if (i % EV == 0) {
+        const int m = i / EV;
+        if (m + KA < NSM) kf[(m + KA) % (KA + 1)] = kread(m + KA);
+        if (m & 1)
+          nxt.s1 = mfma_bf16(kf[m % (KA + 1)], qf[m >> 1], nxt.s1);
+        else
+          nxt.s0 = mfma_bf16(kf[m % (KA + 1)], qf[m >> 1], nxt.s0);
+      }
       // probabilities 2i, 2i+1: k-step ks = i/4, pair jj = i%4 of P^T's B operand
       const int ks = i >> 2, jj = i & 3;
       const f32x16& src = (ks < 2) ? cur.s0 : cur.s1;
@@ -278,25 +308,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     }
     l_run += half_swap_sum(rs);
     // O^T += V^T P^T; consecutive MFMAs update different accumulators. MFMA i
-    // (k-step i/4, d block i%4) takes its V^T operand from two transposing
-    // reads issued VA MFMAs ahead; each MFMA waits for exactly its own reads.
+    // (k-step i / NDB, d block i % NDB) takes its V^T operand from two
+    // transposing reads issued VA MFMAs ahead; each MFMA waits for exactly its
+    // own reads.
     const uint32_t va = lds_addr(vb);
     u32x4 vf[VA + 1];
     auto vread = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      const uint32_t a = va + vr[i & 3];
-      const u32x2 lo = lds_read_tr16<(i >> 2) * 16 * 256>(a);
-      const u32x2 hi = lds_read_tr16<(i >> 2) * 16 * 256 + 8 * 256>(a);
+      const uint32_t a = va + vr[i % NDB];
+      const u32x2 lo = lds_read_tr16<(i / NDB) * 16 * kRow>(a);
+      const u32x2 hi = lds_read_tr16<(i / NDB) * 16 * kRow + 8 * kRow>(a);
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
     static_for<VA>([&](auto ic) { vf[decltype(ic)::value] = vread(ic); });
-    static_for<16>([&](auto ic) {
+    static_for<NPV>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      if constexpr (i + VA < 16) vf[(i + VA) % (VA + 1)] = vread(std::integral_constant<int, i + VA>{});
+      if constexpr (i + VA < NPV) vf[(i + VA) % (VA + 1)] = vread(std::integral_constant<int, i + VA>{});
       // reads issued after MFMA i's own: two per later MFMA already in flight
-      lds_wait_for<2 * ((15 - i) < VA ? (15 - i) : VA)>(vf[i % (VA + 1)]);
-      oacc[i & 3] = mfma_bf16(__builtin_bit_cast(bf16x8, vf[i % (VA + 1)]),
-                              __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
+      constexpr int later = (NPV - 1 - i) < VA ? (NPV - 1 - i) : VA;
+      lds_wait_for<2 * later>(vf[i % (VA + 1)]);
+      oacc[i % NDB] = mfma_bf16(__builtin_bit_cast(bf16x8, vf[i % (VA + 1)]),
+                                __builtin_bit_cast(bf16x8, pw[i / NDB]), oacc[i % NDB]);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -333,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const float inv = 1.f / l_run;
     uint16_t* orow = o + ((size_t)bh * Lq + qrow) * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
         const int d0 = 32 * db + 8 * mm + 4 * g;
@@ -352,7 +384,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale,
                                 int causal, hipStream_t stream) {
-  (void)d;
   const int nqb = (Lq + BM - 1) / BM;
   const int BH = B * Hq;
   const float c = scale * kLog2e;
@@ -361,12 +392,15 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
   auto kk = static_cast<const uint16_t*>(k);
   auto vv = static_cast<const uint16_t*>(v);
   auto oo = static_cast<uint16_t*>(o);
-  if (causal)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, grid, dim3(256), 0, stream, qq, kk, vv, oo, lse,
-                       BH, Hq, Hkv, Lq, Lk, c, nqb);
-  else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, grid, dim3(256), 0, stream, qq, kk, vv, oo,
-                       lse, BH, Hq, Hkv, Lq, Lk, c, nqb);
+#define RF_ATTN_LAUNCH(D_, C_)                                                                 \
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, C_>), grid, dim3(256), 0, stream, qq, kk, vv, oo, \
+                     lse, BH, Hq, Hkv, Lq, Lk, c, nqb)
+  if (d == 64) {
+    if (causal) RF_ATTN_LAUNCH(64, true); else RF_ATTN_LAUNCH(64, false);
+  } else {
+    if (causal) RF_ATTN_LAUNCH(128, true); else RF_ATTN_LAUNCH(128, false);
+  }
+#undef RF_ATTN_LAUNCH
   return hipGetLastError();
 }
 

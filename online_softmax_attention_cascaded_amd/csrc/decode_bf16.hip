@@ -35,11 +35,10 @@
 namespace rf {
 namespace {
 
-constexpr int D = 128;
 constexpr int STEP = 32;                  // keys per wave step
 constexpr int NW = 4;                     // waves per workgroup
-constexpr int kVSlot = STEP * D * 2;      // one step of V rows, 8 KB
-constexpr int kSmem = NW * 2 * kVSlot;    // two slots per wave, 64 KB
+constexpr int kMaxVSlot = STEP * 128 * 2; // one step of V rows at head size 128, 8 KB
+constexpr int kSmem = NW * 2 * kMaxVSlot; // two slots per wave, 64 KB
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -59,24 +58,38 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// V slot layout: row r (a key) holds 256 bytes = 16 chunks of 16 bytes; logical
-// chunk c sits at physical chunk c ^ vswz(r). vswz is even, so the chunk pairs
-// {2n, 2n + 1} (one 16-column block) stay together, and the transposed reads of
-// 32 consecutive lanes (rows 8g + 0..3 and 8g + 8 + 0..3 of a slot, one 32-byte
-// pair each) land on distinct banks.
-__device__ __forceinline__ int vswz(int row) { return 2 * (row & 3) + 8 * ((row >> 3) & 1); }
+// V slot layout: row r (a key) holds 2 D bytes = D / 8 chunks of 16 bytes;
+// logical chunk c sits at physical chunk c ^ vswz(r). vswz is even, so the
+// chunk pairs {2n, 2n + 1} (one 16-column block) stay together; at head size
+// 128 the transposed reads of 32 consecutive lanes (rows 8g + 0..3 and
+// 8g + 8 + 0..3 of a slot, one 32-byte pair each) land on distinct banks.
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return D == 128 ? 2 * (row & 3) + 8 * ((row >> 3) & 1) : 2 * (row & 3);
+}
 
 template <int V>
 using ic = std::integral_constant<int, V>;
 
 struct KRegs {
-  u32x4 k[2][4];  // A operand of S^T = K Q^T: [key block][d step]
+  u32x4 k[2][4];  // A operand of S^T = K Q^T: [key block][d step] (D / 32 d steps used)
 };
 
+// Arrays the lambdas below capture are sized for head size 128 (a size that
+// depends on the template argument keeps the host pass from emitting the
+// kernel); head size 64 uses their leading elements.
+template <int D>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ part_m, float* __restrict__ part_l,
     float* __restrict__ part_acc, int Hq, int Hkv, int Lk, int S, int seg_len, float scale) {
+  constexpr int kRow = 2 * D;              // bytes per K/V row
+  constexpr int kVSlot = STEP * kRow;      // one step of V rows
+  constexpr int NDS = D / 32;              // k-steps of the 16x16x32 score product
+  constexpr int NKL = 2 * NDS;             // K loads per step (per lane)
+  constexpr int NVL = kVSlot / 1024;       // 1 KB V loads per step
+  constexpr int NB = D / 16;               // 16-column blocks of the output
+  constexpr int kChunks = D / 8;           // 16-byte chunks per row
   __shared__ __attribute__((aligned(1024))) char smem[kSmem];
 
   const int s = blockIdx.x % S;
@@ -98,7 +111,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   {
     const uint16_t* qrow = q + ((size_t)b * Hq + hk * G + lq) * D;
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
+    for (int ds = 0; ds < NDS; ++ds) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (lq < G) w = *reinterpret_cast<const u32x4*>(qrow + 32 * ds + 8 * g);
       qf[ds] = __builtin_bit_cast(bf16x8, w);
@@ -111,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   // in flight, and so every wait count, fixed.
   const int kv_end = Lk * D * 2;
   auto soff_of = [&](int step) {
-    return __builtin_amdgcn_readfirstlane(step < nsteps ? (t0 + step * STEP) * 256 : kv_end);
+    return __builtin_amdgcn_readfirstlane(step < nsteps ? (t0 + step * STEP) * kRow : kv_end);
   };
 
   // K row loaded by this lane for key block kb: row i = lq of the block holds key
@@ -120,27 +133,27 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)kv_end);
   int kvo[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) kvo[kb] = (8 * (lq >> 2) + (lq & 3) + 4 * kb) * 256 + 16 * g;
+  for (int kb = 0; kb < 2; ++kb) kvo[kb] = (8 * (lq >> 2) + (lq & 3) + 4 * kb) * kRow + 16 * g;
   auto load_k = [&](int step, KRegs& r) {
     const int soff = soff_of(step);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
+      for (int ds = 0; ds < NDS; ++ds)
         r.k[kb][ds] = buf_load16_stream(krs, kvo[kb] + 64 * ds, soff);
   };
 
-  // V step -> LDS slot: eight 1 KB loads, load i covers rows 4i..4i+3 of the
-  // step; lane l writes physical chunk l % 16 of row 4i + l / 16, so it fetches
-  // the logical chunk (l % 16) ^ vswz(row). Rows past Lk read as zero (their
-  // scores are masked anyway); rows past the segment are real keys whose
-  // weights are 0.
+  // V step -> LDS slot: NVL 1 KB loads, load i covers rows (1024 / kRow) i ..
+  // of the step; lane l writes physical chunk l % kChunks of its row, so it
+  // fetches the logical chunk (l % kChunks) ^ vswz(row). Rows past Lk read as
+  // zero (their scores are masked anyway); rows past the segment are real keys
+  // whose weights are 0.
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)kv_end);
   int vvo[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 4 * i + (lane >> 4);
-    vvo[i] = row * 256 + (((lane & 15) ^ vswz(row)) << 4);
+  for (int i = 0; i < NVL; ++i) {
+    const int row = (1024 / kRow) * i + lane / kChunks;
+    vvo[i] = row * kRow + (((lane % kChunks) ^ vswz<D>(row)) << 4);
   }
   char* vslots = smem + wave * 2 * kVSlot;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)vslots;  // LDS byte address
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     char* dst = vslots + __builtin_amdgcn_readfirstlane(slot * kVSlot);
     const int soff = soff_of(step);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NVL; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + i * 1024), 16, vvo[i], soff, 0,
                                                kStreamPolicy);
   };
@@ -158,15 +171,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   int vto[8];
   {
     const int row = 8 * g + (lq >> 2);
-    const int sw = vswz(row) >> 1;
+    const int sw = vswz<D>(row) >> 1;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) vto[nb] = row * 256 + ((nb ^ sw) << 5) + 8 * (lq & 3);
+    for (int nb = 0; nb < NB; ++nb) vto[nb] = row * kRow + ((nb ^ sw) << 5) + 8 * (lq & 3);
   }
 
   float m_run = kNegInf, l_run = 0.f;  // statistics of query head lq
   f32x4 oacc[8];                       // O[q = 4g + r][d = 16*nb + lq]
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) oacc[nb] = f32x4{};
+  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{};
 
   KRegs ks[3];
   // Prologue, in the order the waits below assume: K(0), V(0), K(1).
@@ -175,8 +188,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   load_k(wave + NW, ks[1]);
 
   // Iteration j handles step wave + NW j with K set j % 3 and V slot j % 2. It
-  // first issues V(j + 1) and K(j + 2), so inside the unrolled loop exactly 24
-  // loads are issued after V(j): K(j + 1), V(j + 1), K(j + 2), eight each. In
+  // first issues V(j + 1) and K(j + 2), so inside the unrolled loop exactly
+  // 2 NKL + NVL loads are issued after V(j): K(j + 1), V(j + 1), K(j + 2). In
   // the tail iterations after the loop some of those K loads feed nothing and
   // the compiler drops them, so the tail waits for all loads instead.
   auto body = [&](auto cset, auto tail_c, int j) {
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     for (int kb = 0; kb < 2; ++kb) {
       f32x4 a = f32x4{};
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) a = mfma16(__builtin_bit_cast(bf16x8, ks[C].k[kb][ds]), qf[ds], a);
+      for (int ds = 0; ds < NDS; ++ds) a = mfma16(__builtin_bit_cast(bf16x8, ks[C].k[kb][ds]), qf[ds], a);
       sacc[kb] = a;
     }
     float mx = kNegInf;
@@ -238,24 +251,29 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     if constexpr (TAIL)
       asm volatile("s_waitcnt vmcnt(0)" : "+v"(l_run) : : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(24)" : "+v"(l_run) : : "memory");
+      asm volatile("s_waitcnt vmcnt(%1)" : "+v"(l_run) : "i"(2 * NKL + NVL) : "memory");
     // ---- O += P V: B operands of the eight d blocks (keys 8g..8g+3, then
     // 8g+4..8g+7, of column 16 nb + lq), read transposed from the slot.
     const uint32_t vs = lds_base + (uint32_t)((j & 1) * kVSlot);
     u32x2 vt[8][2];
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
       vt[nb][0] = tr_read(vs + vto[nb]);
-      vt[nb][1] = tr_read(vs + vto[nb] + 1024);
+      vt[nb][1] = tr_read(vs + vto[nb] + 4 * kRow);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(vt[0][0]), "+v"(vt[0][1]), "+v"(vt[1][0]), "+v"(vt[1][1]),
-                   "+v"(vt[2][0]), "+v"(vt[2][1]), "+v"(vt[3][0]), "+v"(vt[3][1]),
-                   "+v"(vt[4][0]), "+v"(vt[4][1]), "+v"(vt[5][0]), "+v"(vt[5][1]),
-                   "+v"(vt[6][0]), "+v"(vt[6][1]), "+v"(vt[7][0]), "+v"(vt[7][1]));
+    if constexpr (NB == 8)
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(vt[0][0]), "+v"(vt[0][1]), "+v"(vt[1][0]), "+v"(vt[1][1]),
+                     "+v"(vt[2][0]), "+v"(vt[2][1]), "+v"(vt[3][0]), "+v"(vt[3][1]),
+                     "+v"(vt[4][0]), "+v"(vt[4][1]), "+v"(vt[5][0]), "+v"(vt[5][1]),
+                     "+v"(vt[6][0]), "+v"(vt[6][1]), "+v"(vt[7][0]), "+v"(vt[7][1]));
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(vt[0][0]), "+v"(vt[0][1]), "+v"(vt[1][0]), "+v"(vt[1][1]),
+                     "+v"(vt[2][0]), "+v"(vt[2][1]), "+v"(vt[3][0]), "+v"(vt[3][1]));
     // rescale O rows 4g + r by their head's alpha, then accumulate.
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
       const bf16x8 vb = __builtin_bit_cast(
           bf16x8, u32x4{vt[nb][0][0], vt[nb][0][1], vt[nb][1][0], vt[nb][1][1]});
 #pragma unroll
@@ -289,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     sm_l[wave * 16 + lq] = l_run;
   }
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int qh = 4 * g + r;
@@ -399,13 +417,18 @@ __global__ __launch_bounds__(64) void merge_states_kernel(const float* __restric
 hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v, float* part_m,
                                     float* part_l, float* part_acc, int B, int Hq, int Hkv, int Lk,
                                     int d, int S, float scale, hipStream_t stream) {
-  (void)d;
   const int seg_len = (Lk + S - 1) / S;
   dim3 grid(B * Hkv * S);
-  hipLaunchKernelGGL(decode_split_kernel, grid, dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), part_m, part_l, part_acc, Hq, Hkv, Lk, S,
-                     seg_len, scale);
+  if (d == 64)
+    hipLaunchKernelGGL((decode_split_kernel<64>), grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), part_m, part_l, part_acc, Hq, Hkv, Lk, S,
+                       seg_len, scale);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<128>), grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), part_m, part_l, part_acc, Hq, Hkv, Lk, S,
+                       seg_len, scale);
   return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ rf_status rf_attn_fwd(rf_dtype dt, const void* q, const void* k, const void* v, 
                                                B, Hq, Hkv, Lq, Lk, d, scale, causal, stream),
                        "rf_attn_fwd");
   }
-  RF_REQUIRE(d == 128, RF_ERR_UNSUPPORTED, "rf_attn_fwd: bf16 head size %d (need 128)", d);
+  RF_REQUIRE(d == 64 || d == 128, RF_ERR_UNSUPPORTED, "rf_attn_fwd: bf16 head size %d (need 64 or 128)", d);
   RF_REQUIRE((long long)Lk * d * 2 < (1LL << 31), RF_ERR_UNSUPPORTED,
              "rf_attn_fwd: one head's K/V must stay under 2 GiB (Lk=%d)", Lk);
   return from_launch(rf::launch_attn_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, scale, causal, stream),
@@ -88,11 +88,16 @@ rf_status rf_attn_decode_split(rf_dtype dt, const void* q, const void* k, const 
              RF_ERR_INVALID_ARG, "rf_attn_decode_split: pointers must be 16-byte aligned");
   RF_REQUIRE(scale == scale, RF_ERR_INVALID_ARG, "rf_attn_decode_split: scale is NaN");
   RF_REQUIRE((long long)B * Hkv * Lk * d < (1LL << 40), RF_ERR_INVALID_ARG, "rf_attn_decode_split: problem too large");
-  RF_REQUIRE(dt == RF_BF16, RF_ERR_UNSUPPORTED, "rf_attn_decode_split: only bf16 K/V are supported");
-  RF_REQUIRE(d == 128, RF_ERR_UNSUPPORTED, "rf_attn_decode_split: head size %d (need 128)", d);
-  RF_REQUIRE((long long)Lk * d * 2 < (1LL << 31), RF_ERR_UNSUPPORTED,
+  RF_REQUIRE(d == 64 || d == 128, RF_ERR_UNSUPPORTED, "rf_attn_decode_split: head size %d (need 64 or 128)", d);
+  const int esize = dt == RF_BF16 ? 2 : 4;
+  RF_REQUIRE((long long)Lk * d * esize < (1LL << 31), RF_ERR_UNSUPPORTED,
              "rf_attn_decode_split: one head's K/V must stay under 2 GiB (Lk=%d)", Lk);
   RF_REQUIRE(Hq / Hkv <= 16, RF_ERR_UNSUPPORTED, "rf_attn_decode_split: GQA group %d > 16", Hq / Hkv);
+  if (dt == RF_F32)
+    return from_launch(rf::launch_decode_split_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                                   static_cast<const float*>(v), part_m, part_l, part_acc, B,
+                                                   Hq, Hkv, Lk, d, S, scale, stream),
+                       "rf_attn_decode_split");
   return from_launch(rf::launch_decode_split_bf16(q, k, v, part_m, part_l, part_acc, B, Hq, Hkv, Lk,
                                                   d, S, scale, stream),
                      "rf_attn_decode_split");

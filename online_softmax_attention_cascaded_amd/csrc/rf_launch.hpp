@@ -20,6 +20,10 @@ hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
                                     float* part_l, float* part_acc, int B, int Hq, int Hkv, int Lk,
                                     int d, int S, float scale, hipStream_t stream);
 
+hipError_t launch_decode_split_f32(const float* q, const float* k, const float* v, float* part_m,
+                                   float* part_l, float* part_acc, int B, int Hq, int Hkv, int Lk,
+                                   int d, int S, float scale, hipStream_t stream);
+
 hipError_t launch_merge_states(const float* part_m, const float* part_l, const float* part_acc,
                                int rows, int S, int d, int out_bf16, void* o, float* lse,
                                hipStream_t stream);

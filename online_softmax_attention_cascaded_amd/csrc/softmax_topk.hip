@@ -394,13 +394,11 @@ __global__ __launch_bounds__(256) void softmax_topk_e256_k8_kernel(const float* 
 
 hipError_t launch_softmax_topk(const float* logits, int T, int E, int k, int renormalize,
                                float* weights, int32_t* indices, hipStream_t stream) {
-#ifndef RF_TOPK_NO_SORTED
   if (E == 256 && k <= 8) {
     hipLaunchKernelGGL(softmax_topk_e256_k8_kernel, dim3((T + 15) / 16), dim3(256), 0, stream,
                        logits, T, k, renormalize, weights, indices);
     return hipGetLastError();
   }
-#endif
   if (E == 256 && k <= 16) {
     hipLaunchKernelGGL(softmax_topk_e256_kernel, dim3((T + 15) / 16), dim3(256), 0, stream, logits,
                        T, k, renormalize, weights, indices);

@@ -49,13 +49,15 @@ def attention_inputs(seed, B, Hq, Hkv, Lq, Lk, d, dtype=torch.bfloat16):
     return as_bf16(q), as_bf16(k), as_bf16(v)
 
 
-def decode_inputs(seed, B, Hq, Hkv, Lk, d):
-    """q [B,Hq,d], k, v [B,Hkv,Lk,d] ~ N(0,1), bf16 torch CPU tensors."""
+def decode_inputs(seed, B, Hq, Hkv, Lk, d, dtype=torch.bfloat16):
+    """q [B,Hq,d], k, v [B,Hkv,Lk,d] ~ N(0,1), torch CPU tensors of ``dtype``."""
     rng = np.random.default_rng(seed)
-    q = as_bf16(normal(rng, (B, Hq, d)))
-    k = as_bf16(normal(rng, (B, Hkv, Lk, d)))
-    v = as_bf16(normal(rng, (B, Hkv, Lk, d)))
-    return q, k, v
+    q = normal(rng, (B, Hq, d))
+    k = normal(rng, (B, Hkv, Lk, d))
+    v = normal(rng, (B, Hkv, Lk, d))
+    if dtype == torch.float32:
+        return torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)
+    return as_bf16(q), as_bf16(k), as_bf16(v)
 
 
 def mla_inputs(seed, B, H, Lk, dqk=576):

@@ -81,8 +81,9 @@ def attn(lib, dt=BF16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=
         (dict(scale=float("nan")), INVALID),
         (dict(d=96), UNSUPPORTED),
         (dict(dt=F32, d=96), UNSUPPORTED),
-        (dict(d=64), UNSUPPORTED),
+        (dict(d=32), UNSUPPORTED),
         (dict(Lk=1 << 23), UNSUPPORTED),     # one head's K/V reaches 2 GiB
+        (dict(d=64, Lk=1 << 24), UNSUPPORTED),
     ],
 )
 def test_attn_validation(lib, kw, expect):
@@ -109,14 +110,25 @@ def decode(lib, dt=BF16, q=FAKE, k=FAKE, v=FAKE, m=FAKE, l=FAKE, acc=FAKE, B=1, 
         (dict(Lk=0), INVALID),
         (dict(acc=None), INVALID),
         (dict(k=MISALIGNED), INVALID),
-        (dict(dt=F32), UNSUPPORTED),
-        (dict(d=64), UNSUPPORTED),
+        (dict(dt=7), INVALID),
+        (dict(scale=float("nan")), INVALID),
+        (dict(d=96), UNSUPPORTED),
+        (dict(dt=F32, d=32), UNSUPPORTED),
         (dict(Hq=34, Hkv=2), UNSUPPORTED),
+        (dict(dt=F32, Hq=34, Hkv=2), UNSUPPORTED),
         (dict(Lk=1 << 23), UNSUPPORTED),     # one head's K/V reaches 2 GiB
+        (dict(dt=F32, Lk=1 << 22), UNSUPPORTED),
+        (dict(dt=F32, d=64, Lk=1 << 23), UNSUPPORTED),
     ],
 )
 def test_decode_validation(lib, kw, expect):
     assert decode(lib, **kw) == expect
+    assert lib.rf_last_error().startswith(b"rf_attn_decode_split")
+
+
+def test_decode_empty_is_ok_without_pointers(lib):
+    for dt in (F32, BF16):
+        assert decode(lib, dt=dt, q=None, k=None, v=None, m=None, l=None, acc=None, B=0) == OK
 
 
 def mla(lib, q=FAKE, kv=FAKE, m=FAKE, l=FAKE, acc=FAKE, B=2, H=16, Lk=100, Dqk=576, Dv=512, S=4,

@@ -69,39 +69,66 @@ def test_partials_and_merge_small(B, Hq, Hkv, Lk, S):
     assert np.abs(np32(lse) - lse_ref[:, :, 0]).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
 
 
-@pytest.fixture(scope="module")
-def decode_config():
-    """The decode workload: B=8, Hq=32, Hkv=8 (GQA 4:1), Lk=32768, d=128, bf16."""
-    q, k, v = inputs.decode_inputs(2, 8, 32, 8, 32768, 128)
-    return q, k, v, q.to(DEV), k.to(DEV), v.to(DEV)
+def _check_partials(m, l, acc, m_ref, l_ref, acc_ref, acc_bar):
+    m, l, acc = np32(m), np32(l), np32(acc)
+    empty = np.isinf(m_ref)
+    assert np.array_equal(np.isinf(m), empty)
+    assert np.all(l[empty] == 0) and np.all(acc[empty] == 0)
+    fin = ~empty
+    assert np.abs(m[fin] - m_ref[fin]).max() <= 1e-5 * max(1, np.abs(m_ref[fin]).max())
+    assert normwise(l[fin], l_ref[fin]) <= 1e-5
+    assert normwise(acc[fin], acc_ref[fin]) <= acc_bar
 
 
-@pytest.mark.parametrize("S", [1, 4, 8, 16, 64])
-def test_decode_config_sampled(decode_config, S):
-    q, k, v, qd, kd, vd = decode_config
-    print_case(test="decode_full", S=S)
-    scale = 1 / math.sqrt(128)
-    o, lse, (m, l, acc) = rf.attn_decode(qd, kd, vd, scale, S)
-    o, lse, m, l, acc = np32(o), np32(lse), np32(m), np32(l), np32(acc)
-    assert np.isfinite(o).all()
-    for b, h in [(0, 0), (3, 13), (7, 31)]:
-        hk = h // 4
-        qs, ks, vs = q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1]
-        m_ref, l_ref, acc_ref = oracle.decode_partials(qs, ks, vs, scale, S)
-        assert np.abs(m[b, h] - m_ref[0, 0]).max() <= 1e-5 * np.abs(m_ref).max()
-        assert normwise(l[b, h], l_ref[0, 0]) <= 1e-5
-        assert normwise(acc[b, h], acc_ref[0, 0]) <= 1e-4
-        o_ref, lse_ref = oracle.attention(qs[:, :, None], ks, vs, scale)
-        assert_bf16_attention(o[b, h], o_ref[0, 0, 0], lse[b, h], lse_ref[0, 0, 0], what=f"b={b} h={h}")
+@pytest.mark.parametrize(
+    "B,Hq,Hkv,Lk,S",
+    [
+        (1, 4, 1, 3000, 1),
+        (2, 8, 2, 3000, 4),
+        (2, 8, 2, 777, 64),       # segments of 13 keys, ragged
+        (1, 4, 1, 5, 4),          # an empty segment
+        (1, 16, 1, 513, 3),       # G = 16
+        (2, 6, 2, 96, 2),         # G = 3
+    ],
+)
+def test_head64_partials_and_merge(B, Hq, Hkv, Lk, S):
+    """Head size 64 on the bf16 MFMA path."""
+    print_case(test="decode_head64", B=B, Hq=Hq, Hkv=Hkv, Lk=Lk, S=S)
+    d = 64
+    q, k, v = inputs.decode_inputs(15, B, Hq, Hkv, Lk, d)
+    scale = 1 / math.sqrt(d)
+    o, lse, (m, l, acc) = rf.attn_decode(q.to(DEV), k.to(DEV), v.to(DEV), scale, S,
+                                         out_dtype=torch.float32)
+    _check_partials(m, l, acc, *oracle.decode_partials(q, k, v, scale, S), acc_bar=1e-4)
+    o_ref, lse_ref = oracle.attention(q[:, :, None], k, v, scale)
+    assert normwise(np32(o), o_ref[:, :, 0]) <= 1e-4
+    assert np.abs(np32(lse) - lse_ref[:, :, 0]).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
 
 
-def test_cross_segment_consistency(decode_config):
-    """Different segment counts merge to the same answer (fp32 output)."""
-    q, k, v, qd, kd, vd = decode_config
-    outs = [np32(rf.attn_decode(qd[:2], kd[:2], vd[:2], 0.1, S, out_dtype=torch.float32)[0])
-            for S in (1, 4, 16, 64)]
-    for o in outs[1:]:
-        assert normwise(o, outs[0]) <= 1e-4
+@pytest.mark.parametrize(
+    "B,Hq,Hkv,Lk,d,S",
+    [
+        (1, 4, 1, 3000, 128, 1),
+        (2, 8, 2, 777, 128, 4),   # ragged last segment and chunk
+        (1, 4, 1, 5, 128, 4),     # an empty segment
+        (1, 4, 4, 100, 64, 64),   # many trailing empty segments, G = 1
+        (1, 16, 1, 513, 64, 3),   # G = 16
+        (2, 6, 2, 96, 64, 2),     # G = 3
+        (2, 8, 2, 4096, 64, 16),
+    ],
+)
+def test_fp32_partials_and_merge(B, Hq, Hkv, Lk, d, S):
+    """fp32 K/V: every step in fp32, bar 1e-5 normwise for the states and the
+    merged output."""
+    print_case(test="decode_fp32", B=B, Hq=Hq, Hkv=Hkv, Lk=Lk, d=d, S=S)
+    q, k, v = inputs.decode_inputs(16, B, Hq, Hkv, Lk, d, dtype=torch.float32)
+    scale = 1 / math.sqrt(d)
+    o, lse, (m, l, acc) = rf.attn_decode(q.to(DEV), k.to(DEV), v.to(DEV), scale, S,
+                                         out_dtype=torch.float32)
+    _check_partials(m, l, acc, *oracle.decode_partials(q, k, v, scale, S), acc_bar=FP32_REL)
+    o_ref, lse_ref = oracle.attention(q[:, :, None], k, v, scale)
+    assert normwise(np32(o), o_ref[:, :, 0]) <= FP32_REL
+    assert np.abs(np32(lse) - lse_ref[:, :, 0]).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
 
 
 # ---------------------------------------------------------------- merge alone

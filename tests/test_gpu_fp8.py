@@ -93,24 +93,6 @@ def test_gemm_small(M, N, K):
     assert rel_fro(np32(c), c_ref) <= 5e-3
 
 
-def test_fp8_config_sampled():
-    """M=4096, N=4096, K=7168, 0.1 % outliers x50 in A: all quantised codes bit-exact,
-    the GEMM checked on 64 sampled rows against the exact fp64 oracle."""
-    print_case(test="fp8_full")
-    M, N, K = 4096, 4096, 7168
-    a, bsrc = inputs.quant_inputs(4, M, N, K)
-    bq, bs = rf.absmax_quant_fp8(bsrc.to(DEV))
-    c, aq, sa = rf.absmax_quant_gemm_fp8(a.to(DEV), bq, bs)
-    rows = np.random.default_rng(0).choice(M, 64, replace=False)
-    aq_ref, sa_ref = oracle.absmax_quant(a[rows].float().numpy())
-    assert np.array_equal(aq.cpu().numpy()[rows], aq_ref)
-    assert np.array_equal(sa.cpu().numpy()[rows], sa_ref)
-    bq_ref, bs_ref = oracle.absmax_quant(bsrc[:512].float().numpy())
-    assert np.array_equal(bq[:512].cpu().numpy(), bq_ref)
-    c_ref = oracle.quant_gemm(aq_ref, sa_ref, bq.cpu().numpy(), bs.cpu().numpy())
-    assert rel_fro(np32(c)[rows], c_ref) <= FP8_REL_FRO
-
-
 # ---- one-pass form with a running per-row scale (K tiles of 64 columns)
 
 K_TILE = 64
@@ -152,24 +134,3 @@ def test_running_scale_growth_and_zero_rows():
     assert rel_fro(c, c_ref) <= 5e-3
     for r in (2, 3, 4):
         assert rel_fro(c[r], c_ref[r]) <= 5e-3
-
-
-def test_running_scale_config_sampled():
-    """M=4096, N=4096, K=7168 with the FP8 workload's outliers: 64 sampled rows
-    against the one-pass oracle; the deviation from the final-scale path is the
-    quantisation of the early K tiles (reported, not gated beyond 3e-2)."""
-    print_case(test="gemm_running_full")
-    M, N, K = 4096, 4096, 7168
-    a, bsrc = inputs.quant_inputs(4, M, N, K)
-    bq, bs = rf.absmax_quant_fp8(bsrc.to(DEV))
-    c, sa = rf.absmax_quant_gemm_fp8_running(a.to(DEV), bq, bs)
-    rows = np.random.default_rng(1).choice(M, 64, replace=False)
-    x = a[rows].float().numpy()
-    c_ref = oracle.quant_gemm_running_scale(x, bq.cpu().numpy(), bs.cpu().numpy(), K_TILE)
-    assert rel_fro(np32(c)[rows], c_ref) <= 5e-3
-    aq_f, sa_f = oracle.absmax_quant(x)
-    assert np.array_equal(sa.cpu().numpy()[rows], sa_f)
-    c_final = oracle.quant_gemm(aq_f, sa_f, bq.cpu().numpy(), bs.cpu().numpy())
-    dev_final = rel_fro(c_ref, c_final)
-    print(f"running-scale vs final-scale quantisation: {dev_final:.4f} relative Frobenius")
-    assert dev_final <= FP8_REL_FRO

@@ -1,0 +1,244 @@
+"""Full-size parity: every output of each measured workload, in the launch
+configuration the bench times, compared element by element with the fp64
+oracle (the oracle finishes each workload in seconds to tens of seconds on the
+host). Bars:
+
+* prefill (B=4, H=32, L=2048, d=128, bf16): every (batch, head) slice within
+  2e-2 max absolute error and 1e-2 relative Frobenius error on O, 1e-3 on lse;
+* decode (B=8, Hq=32, Hkv=8, Lk=32768, d=128, bf16): every partial state of
+  every row at every segment count -- m to 1e-5 relative, l to 1e-5 relative
+  per element, acc to 1e-4 of its row's largest entry -- and every merged row
+  (bf16 output as timed, and fp32 output to 1e-4 of the row's largest entry);
+* multi-latent decode (32 sequences, 16 heads, 8192 latent rows): every row
+  of both launch forms at every timed segment count, as decode;
+* FP8 (M=N=4096, K=7168): every code and scale of A and B bit-exact, and every
+  entry of C within the rounding bound of its own arithmetic (below);
+* running-scale FP8: every entry within the same kind of bound against the
+  one-pass oracle.
+"""
+
+import math
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import online_softmax_attention_cascaded_amd as rf
+from online_softmax_attention_cascaded_amd import inputs
+from gpu_util import DEV, BF16_ABS, BF16_REL_FRO, LSE_ABS, needs_gpu, np32, print_case, rel_fro
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _row_normwise(got, ref):
+    """max |got - ref| / max |ref| along the last axis, for every row."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.abs(ref).max(axis=-1)
+    return np.abs(got - ref).max(axis=-1) / np.where(scale > 0, scale, 1.0)
+
+
+# ------------------------------------------------------------------ prefill
+
+
+@pytest.fixture(scope="module")
+def prefill():
+    B, H, L, d = 4, 32, 2048, 128
+    q, k, v = inputs.attention_inputs(1, B, H, H, L, L, d)
+    return q, k, v, q.to(DEV), k.to(DEV), v.to(DEV)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_every_slice(prefill, causal):
+    q, k, v, qd, kd, vd = prefill
+    print_case(test="prefill_full", causal=causal)
+    scale = 1 / math.sqrt(q.shape[-1])
+    o, lse = rf.attn_fwd(qd, kd, vd, scale, causal=causal)
+    o, lse = np32(o), np32(lse)
+    worst = [0.0, 0.0, 0.0]
+    t = time.time()
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            o_ref, lse_ref = oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1],
+                                              v[b:b + 1, h:h + 1], scale, causal=causal)
+            err = np.abs(o[b, h] - o_ref[0, 0]).max()
+            fro = rel_fro(o[b, h], o_ref[0, 0])
+            lerr = np.abs(lse[b, h] - lse_ref[0, 0]).max()
+            assert err <= BF16_ABS and fro <= BF16_REL_FRO and lerr <= LSE_ABS, (b, h, err, fro, lerr)
+            worst = [max(worst[0], err), max(worst[1], fro), max(worst[2], lerr)]
+    print(f"128 slices in {time.time() - t:.1f} s: max abs {worst[0]:.2e}, rel fro {worst[1]:.2e}, "
+          f"lse {worst[2]:.2e}")
+
+
+# ------------------------------------------------------------------- decode
+
+
+@pytest.fixture(scope="module")
+def decode():
+    B, Hq, Hkv, Lk, d = 8, 32, 8, 32768, 128
+    q, k, v = inputs.decode_inputs(2, B, Hq, Hkv, Lk, d)
+    dev = q.to(DEV), k.to(DEV), v.to(DEV)
+    q64, k64, v64 = (t.to(torch.float64).numpy() for t in (q, k, v))   # exact upcast, once
+    scale = 1 / math.sqrt(d)
+    o_ref, lse_ref = oracle.attention(q64[:, :, None], k64, v64, scale)
+    return dict(host=(q64, k64, v64), dev=dev, scale=scale, o_ref=o_ref[:, :, 0], lse_ref=lse_ref[:, :, 0])
+
+
+def _check_states(m, l, acc, m_ref, l_ref, acc_ref):
+    m, l, acc = np32(m), np32(l), np32(acc)
+    empty = np.isinf(m_ref)
+    assert np.array_equal(np.isinf(m), empty)
+    assert np.all(l[empty] == 0) and np.all(acc[empty] == 0)
+    fin = ~empty
+    merr = np.abs(m[fin] - m_ref[fin]) / np.maximum(1, np.abs(m_ref[fin]))
+    lerr = np.abs(l[fin] - l_ref[fin]) / l_ref[fin]
+    aerr = _row_normwise(acc[fin], acc_ref[fin])
+    assert merr.max() <= 1e-5, merr.max()
+    assert lerr.max() <= 1e-5, lerr.max()
+    assert aerr.max() <= 1e-4, aerr.max()
+    return merr.max(), lerr.max(), aerr.max()
+
+
+@pytest.mark.parametrize("S", [1, 4, 8, 16, 64])
+def test_decode_every_row(decode, S):
+    print_case(test="decode_full", S=S)
+    (q64, k64, v64), (qd, kd, vd), scale = decode["host"], decode["dev"], decode["scale"]
+    o, lse, (m, l, acc) = rf.attn_decode(qd, kd, vd, scale, S)               # bf16 output, as timed
+    o32, lse32 = rf.merge_states(m, l, acc, out_dtype=torch.float32)
+    worst = _check_states(m, l, acc, *oracle.decode_partials(q64, k64, v64, scale, S))
+    o_ref, lse_ref = decode["o_ref"], decode["lse_ref"]
+    o, o32 = np32(o), np32(o32)
+    assert np.abs(o - o_ref).max() <= BF16_ABS
+    assert (np.abs(o - o_ref) <= 2 ** -8 * np.abs(o_ref) + 1e-4 * np.abs(o_ref).max(-1, keepdims=True)).all()
+    assert _row_normwise(o32, o_ref).max() <= 1e-4
+    for got in (np32(lse), np32(lse32)):
+        assert np.abs(got - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+    print(f"S={S}: m {worst[0]:.1e} l {worst[1]:.1e} acc {worst[2]:.1e} "
+          f"o32 {_row_normwise(o32, o_ref).max():.1e}")
+
+
+def test_decode_segment_counts_agree(decode):
+    """Different segment counts merge to the same answer (fp32 output)."""
+    qd, kd, vd = decode["dev"]
+    outs = [np32(rf.attn_decode(qd, kd, vd, decode["scale"], S, out_dtype=torch.float32)[0])
+            for S in (1, 4, 16, 64)]
+    for o in outs[1:]:
+        assert _row_normwise(o, outs[0]).max() <= 1e-4
+
+
+# --------------------------------------------------------- multi-latent decode
+
+DQK, DV = 576, 512
+
+
+@pytest.fixture(scope="module")
+def mla():
+    B, H, Lk = 32, 16, 8192
+    q, kv = inputs.mla_inputs(9, B, H, Lk)
+    q64 = q.to(torch.float64).numpy()
+    lat = kv[:, None].to(torch.float64).numpy()          # [B, 1, Lk, 576]: one shared latent head
+    scale = 1 / math.sqrt(DQK)
+    o_ref, lse_ref = oracle.attention(q64[:, :, None], lat, lat[..., :DV], scale)
+    return dict(host=(q64, lat), dev=(q.to(DEV), kv.to(DEV)), scale=scale, o_ref=o_ref[:, :, 0],
+                lse_ref=lse_ref[:, :, 0])
+
+
+@pytest.mark.parametrize("S", [8, 16, 32])
+def test_mla_every_row(mla, S):
+    print_case(test="mla_full", S=S)
+    (q64, lat), (qd, kvd), scale = mla["host"], mla["dev"], mla["scale"]
+    o, lse, (m, l, acc) = rf.mla_decode(qd, kvd, scale, S, out_dtype=torch.float32)
+    _check_states(m, l, acc, *oracle.decode_partials(q64, lat, lat[..., :DV], scale, S))
+    of, lsef, _ = rf.mla_decode(qd, kvd, scale, S, out_dtype=torch.float32, fused=True)
+    o_ref, lse_ref = mla["o_ref"], mla["lse_ref"]
+    for got_o, got_lse in ((o, lse), (of, lsef)):
+        assert _row_normwise(np32(got_o), o_ref).max() <= 1e-4
+        assert np.abs(np32(got_lse) - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+    ob, _, _ = rf.mla_decode(qd, kvd, scale, S, fused=True)                 # bf16 output, as timed
+    ob = np32(ob)
+    assert (np.abs(ob - o_ref) <= 2 ** -8 * np.abs(o_ref) + 1e-4 * np.abs(o_ref).max(-1, keepdims=True)).all()
+
+
+# ---------------------------------------------------------------------- FP8
+#
+# Bound on one entry of C. The kernel forms sum_k a_k b_k of exact e4m3 products
+# in fp32 (each of the K additions rounds with relative error <= 2^-24 of a
+# partial sum, and every partial sum is <= sum_k |a_k b_k|), scales it by s_i
+# and t_j (two fp32 roundings) and rounds to bf16 (<= 2^-8 relative). So
+#   |c - c_ref| <= 2^-8 |c_ref| + (K + 4) 2^-23 s_i t_j sum_k |a_k b_k|,
+# where 2^-23 (twice the unit roundoff) also absorbs the bf16 rounding of the
+# accumulated error and the scale roundings. c_ref is exact (see oracle.quant).
+
+M_, N_, K_ = 4096, 4096, 7168
+K_TILE = 64
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    a, bsrc = inputs.quant_inputs(4, M_, N_, K_)
+    bq, bs = rf.absmax_quant_fp8(bsrc.to(DEV))
+    c, aq, sa = rf.absmax_quant_gemm_fp8(a.to(DEV), bq, bs)
+    t = time.time()
+    aq_ref, sa_ref = oracle.absmax_quant(a.float().numpy())
+    bq_ref, bs_ref = oracle.absmax_quant(bsrc.float().numpy())
+    print(f"oracle quantiser on A and B: {time.time() - t:.1f} s", flush=True)
+    return dict(a=a, gpu=(np32(c), aq.cpu().numpy(), sa.cpu().numpy(), bq.cpu().numpy(), bs.cpu().numpy()),
+                ref=(aq_ref, sa_ref, bq_ref, bs_ref), dev=(bq, bs))
+
+
+def test_fp8_every_code_and_scale(fp8):
+    print_case(test="fp8_full_codes")
+    _, aq, sa, bq, bs = fp8["gpu"]
+    aq_ref, sa_ref, bq_ref, bs_ref = fp8["ref"]
+    assert np.array_equal(sa, sa_ref) and np.array_equal(bs, bs_ref)
+    for got, ref, name in ((aq, aq_ref, "A"), (bq, bq_ref, "B")):
+        bad = np.argwhere(got != ref)
+        assert len(bad) == 0, f"{name}: {len(bad)} codes differ, first {bad[:3].tolist()}"
+
+
+def _abs_codes(codes):
+    return np.abs(oracle.e4m3_decode(codes))
+
+
+def test_fp8_every_entry_of_c(fp8):
+    print_case(test="fp8_full_gemm")
+    c, _, _, _, _ = fp8["gpu"]
+    aq_ref, sa_ref, bq_ref, bs_ref = fp8["ref"]
+    c_ref = oracle.quant_gemm(aq_ref, sa_ref, bq_ref, bs_ref)
+    st = sa_ref.astype(np.float64)[:, None] * bs_ref.astype(np.float64)[None, :]
+    mag = st * (_abs_codes(aq_ref) @ _abs_codes(bq_ref).T)                  # s_i t_j sum |a b|
+    tol = 2.0 ** -8 * np.abs(c_ref) + (K_ + 4) * 2.0 ** -23 * mag
+    err = np.abs(c - c_ref)
+    bad = np.argwhere(err > tol)
+    assert len(bad) == 0, f"{len(bad)} entries outside the bound, first {bad[:3].tolist()}"
+    print(f"largest error / bound {np.max(err / np.where(tol > 0, tol, 1)):.3f}; "
+          f"relative Frobenius {rel_fro(c, c_ref):.2e}")
+
+
+def test_running_scale_every_entry(fp8):
+    """One pass with a running per-row scale. Besides the bound above, each
+    time a row's scale grows the fp32 accumulator is multiplied by a rounded
+    fp32 factor (at most K / 64 times), so the bound takes 3 * K / 64 more
+    units; its magnitude term is the same one-pass sum over absolute values
+    (the oracle run on |A| and |B|: the codes of |x| are the magnitudes of the
+    codes of x, and the scales are the same)."""
+    print_case(test="fp8_running_full")
+    a = fp8["a"]
+    bqd, bsd = fp8["dev"]
+    c, sa = rf.absmax_quant_gemm_fp8_running(a.to(DEV), bqd, bsd)
+    c, sa = np32(c), sa.cpu().numpy()
+    _, _, bq_ref, bs_ref = fp8["ref"]
+    _, sa_ref, _, _ = fp8["ref"]
+    assert np.array_equal(sa, sa_ref)
+    x = a.float().numpy()
+    t = time.time()
+    c_ref = oracle.quant_gemm_running_scale(x, bq_ref, bs_ref, K_TILE)
+    mag = oracle.quant_gemm_running_scale(np.abs(x), bq_ref & 0x7F, bs_ref, K_TILE)
+    print(f"one-pass oracle twice: {time.time() - t:.1f} s", flush=True)
+    tol = 2.0 ** -8 * np.abs(c_ref) + (K_ + 3 * K_ // K_TILE + 4) * 2.0 ** -23 * mag
+    err = np.abs(c - c_ref)
+    bad = np.argwhere(err > tol)
+    assert len(bad) == 0, f"{len(bad)} entries outside the bound, first {bad[:3].tolist()}"
+    print(f"largest error / bound {np.max(err / np.where(tol > 0, tol, 1)):.3f}")

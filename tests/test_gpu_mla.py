@@ -109,25 +109,6 @@ def test_mla_large_scores():
     _check(2, 16, 2000, 3, 1.0)
 
 
-@pytest.mark.parametrize("S", [8, 16, 32])
-def test_mla_config_sampled(S):
-    """The measured workload, B=32 sequences, H=16, Lk=8192 latent rows of 576,
-    in the launch configuration the bench times; three sequences checked
-    against the oracle, every output finite."""
-    print_case(test="mla_config", S=S)
-    B, H, Lk = 32, 16, 8192
-    scale = 1 / math.sqrt(DQK)
-    q, kv = inputs.mla_inputs(9, B, H, Lk)
-    o, lse, _ = rf.mla_decode(q.to(DEV), kv.to(DEV), scale, S, out_dtype=torch.float32)
-    o, lse = np32(o), np32(lse)
-    assert np.isfinite(o).all() and np.isfinite(lse).all()
-    for b in (0, 13, 31):
-        lat = kv[b:b + 1, None]
-        o_ref, lse_ref = oracle.attention(q[b:b + 1, :, None], lat, lat[..., :DV], scale)
-        assert normwise(o[b], o_ref[0, :, 0]) <= 1e-4
-        assert np.abs(lse[b] - lse_ref[0, :, 0]).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
-
-
 def test_mla_deterministic():
     q, kv = (t.to(DEV) for t in inputs.mla_inputs(3, 2, 32, 1500))
     a = rf.mla_decode(q, kv, 0.05, 5)
