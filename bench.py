@@ -50,7 +50,7 @@ def rotated(t, n=ROW_ROTATE):
     other addresses (row results are unchanged, only their order)."""
     return [t] + [t.roll(7 * r, dims=0).contiguous() for r in range(1, n)]
 SOFTMAX_E = (1024, 2048, 4096, 8192)
-DECODE_SEGMENTS = (4, 8, 16, 64)
+DECODE_SEGMENTS = (1, 4, 8, 16, 64)
 ROUTING_ROTATE = 20
 FP8_ROTATE = 5
 
@@ -105,51 +105,88 @@ def read_traffic():
     return out
 
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle as it stands, timed on this host on a bounded sample of the same
-    workloads: whole (batch, head) slices of the non-causal prefill and whole
-    query rows of the S=16 decode, each run until about half the budget is spent."""
-    import numpy as np
+def _cpu_worker(args):
+    """One pool worker: the oracle on its own (batch, head) prefill slice, then on
+    its own query rows of the S=16 decode, each for half the budget, with BLAS
+    held to one thread."""
+    wid, budget_s = args
     import threadpoolctl
 
     import oracle
     from online_softmax_attention_cascaded_amd import inputs
 
-    P = PREFILL
-    q, k, v = inputs.attention_inputs(1, 1, 2, 2, P["L"], P["L"], P["d"])
-    scale = 1 / math.sqrt(P["d"])
-    n_heads, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s / 2 or n_heads == 0:
-        h = n_heads % 2
-        oracle.attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], scale)
-        n_heads += 1
-    t_pre = time.perf_counter() - t0
-    pre_tflops = n_heads * 4.0 * P["L"] * P["L"] * P["d"] / t_pre / 1e12
+    with threadpoolctl.threadpool_limits(limits=1):
+        P = PREFILL
+        q, k, v = inputs.attention_inputs(1 + wid, 1, 1, 1, P["L"], P["L"], P["d"])
+        scale = 1 / math.sqrt(P["d"])
+        oracle.attention(q, k, v, scale)            # untimed: first-touch of the work arrays
+        n_heads, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget_s / 2 or n_heads == 0:
+            oracle.attention(q, k, v, scale)
+            n_heads += 1
+        t_pre = time.perf_counter() - t0
+        Dc = DECODE
+        qd, kd, vd = inputs.decode_inputs(2 + wid, 1, 4, 1, Dc["Lk"], Dc["d"])
+        oracle.decode_partials(qd, kd, vd, scale, 16)
+        n_rows, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget_s / 2 or n_rows == 0:
+            m, l, acc = oracle.decode_partials(qd, kd, vd, scale, 16)
+            oracle.merge_states(m, l, acc)
+            n_rows += qd.shape[1]
+        t_dec = time.perf_counter() - t0
+    return n_heads, t_pre, n_rows, t_dec
 
-    Dc = DECODE
-    qd, kd, vd = inputs.decode_inputs(2, 1, 4, 1, Dc["Lk"], Dc["d"])
-    n_rows, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s / 2 or n_rows == 0:
-        m, l, acc = oracle.decode_partials(qd, kd, vd, scale, 16)
-        oracle.merge_states(m, l, acc)
-        n_rows += qd.shape[1]
-    t_dec = time.perf_counter() - t0
+
+def _host_description():
+    import platform
+
+    import numpy as np
+    import threadpoolctl
+
+    model = platform.processor() or "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpoolctl.threadpool_info()
+            if i.get("user_api") == "blas"]
+    return model, np.__version__, ", ".join(blas) or "none found"
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands, timed on this host on a bounded sample of the same
+    workloads: a pool of one process per usable core (at most 16), BLAS held to
+    one thread in each, every worker running whole (batch, head) slices of the
+    non-causal prefill and then whole query rows of the S=16 decode for half the
+    budget each (after one untimed call of each). Throughputs are the sums over the workers. Called before this
+    process touches the GPU, so the forked workers inherit no device state."""
+    import multiprocessing as mp
+
+    workers = max(1, min(os.cpu_count() or 1, len(os.sched_getaffinity(0)), 16))
+    with mp.get_context("fork").Pool(workers) as pool:
+        res = pool.map(_cpu_worker, [(w, budget_s) for w in range(workers)])
+    P, Dc = PREFILL, DECODE
+    n_heads = sum(r[0] for r in res)
+    n_rows = sum(r[2] for r in res)
+    pre_tflops = sum(r[0] * 4.0 * P["L"] * P["L"] * P["d"] / r[1] for r in res) / 1e12
     # Bytes of the full workload per query row: its share of K/V (one GQA group of 4
     # rows reads one K/V head) plus q and O.
     bytes_per_row = (2 * Dc["Lk"] * Dc["d"] * 2) / (Dc["Hq"] // Dc["Hkv"]) + 2 * Dc["d"] * 2
-    dec_gbs = n_rows * bytes_per_row / t_dec / 1e9
-
-    blas = [i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
-    cores = max(blas) if blas else 1
+    dec_gbs = sum(r[2] * bytes_per_row / r[3] for r in res) / 1e9
+    model, np_version, blas = _host_description()
     value = 0.5 * (pre_tflops / PEAK_BF16_TFLOPS + dec_gbs / PEAK_HBM_GBS) * 100
     return {
         "value": value,
         "unit": "% of MI355X peak (mean of prefill/bf16-MFMA and decode/HBM fractions)",
-        "cores": cores,
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: {n_heads} (batch, head) slices of the non-causal prefill "
-                   f"(L=2048, d=128) in {t_pre:.1f} s and {n_rows} query rows of the S=16 decode "
-                   f"(Lk=32768) in {t_dec:.1f} s; BLAS threads {cores}, numpy elementwise single-threaded"),
+        "sample": (f"fp64 numpy oracle in {workers} processes, one BLAS thread each, about "
+                   f"{budget_s:.0f} s: {n_heads} (batch, head) slices of the non-causal prefill "
+                   f"(L=2048, d=128) and {n_rows} query rows of the S=16 decode (Lk=32768)"),
+        "host": {"cpu": model, "numpy": np_version, "blas": blas},
         "prefill_tflops": pre_tflops,
         "decode_gbs": dec_gbs,
     }
@@ -181,11 +218,17 @@ def main():
         import __graft_entry__
 
         __graft_entry__.build()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
 
     def progress(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        progress("timing the oracle on the host (before the GPU is touched)")
+        cpu = cpu_baseline()
+        progress(f"oracle on {cpu['cores']} host cores: {cpu['value']:.5f} % of peak")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
 
     if args.calibrate_copy:
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
@@ -691,9 +734,8 @@ def main():
         vendor["fp8_gemm"] = None
     result["vendor"] = vendor
     progress("vendor kernels timed for context")
-    if not args.no_cpu_baseline:
-        progress("timing the oracle on the host")
-        result["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result))
 
 

@@ -27,7 +27,9 @@
  *   - Tensor pointers are DEVICE pointers on the current HIP device, row-major
  *     and contiguous, 16-byte aligned unless stated otherwise. The caller
  *     allocates and owns every buffer (including workspaces); the library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing. The only state kept between calls is a per-device
+ *     cache of the compute-unit count (read once, used to pick a launch
+ *     shape).
  *   - Outputs must not alias inputs.
  *   - Calls only enqueue work on `stream` (0 = the null stream) and return.
  *     All arguments are validated before anything is enqueued, so a call that

@@ -322,14 +322,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
       mw[w] = sm_m[w * 16 + qh];
       ms = fmaxf(ms, mw[w]);
     }
+    // No shortcut for ms = -inf: every weight is then 0, and 0 * l keeps a NaN
+    // that reached l (scores that are all NaN leave the max at -inf).
     float l = 0.f, acc = 0.f;
-    if (ms != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float wt = (mw[w] == kNegInf) ? 0.f : fast_exp2((mw[w] - ms) * kLog2e);
-        l += wt * sm_l[w * 16 + qh];
-        acc += wt * sm_acc[(w * 16 + qh) * D + d];
-      }
+    for (int w = 0; w < NW; ++w) {
+      const float wt = (mw[w] == kNegInf) ? 0.f : fast_exp2((mw[w] - ms) * kLog2e);
+      l += wt * sm_l[w * 16 + qh];
+      acc += wt * sm_acc[(w * 16 + qh) * D + d];
     }
     const size_t row = ((size_t)b * Hq + hk * G + qh) * S + s;
     part_acc[row * D + d] = acc;
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(64) void merge_states_kernel(const float* __restric
     for (int e = 0; e < 4; ++e) a2[e] = __shfl_xor(acc[e], 32, kWave);
     fold_state(m, l, acc, m2, l2, a2);
     if (h == 0 && act) {
-      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+      const float inv = (l > 0.f) ? 1.f / l : (l == 0.f ? 0.f : l);  // a NaN in l stays NaN
       acc *= inv;
       if (out_bf16) {
         const u32x2 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(64) void merge_states_kernel(const float* __restric
         *reinterpret_cast<f32x4*>(static_cast<float*>(o) + row * d + col) = acc;
       }
     }
-    if (lse && lane == 0 && c0 == 0) lse[row] = (m == kNegInf) ? kNegInf : m + logf(l);
+    if (lse && lane == 0 && c0 == 0) lse[row] = (m == kNegInf && l == 0.f) ? kNegInf : m + logf(l);
   }
 }
 

@@ -143,14 +143,14 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
       mw[w] = sm_m[w][h];
       ms = fmaxf(ms, mw[w]);
     }
+    // No shortcut for ms = -inf: every weight is then 0, and 0 * l keeps a NaN
+    // that reached l.
     float l = 0.f, a = 0.f;
-    if (ms != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float wt = (mw[w] == kNegInf) ? 0.f : fast_exp2((mw[w] - ms) * kLog2e);
-        l += wt * sm_l[w][h];
-        a += wt * sm_acc[w][h][d];
-      }
+    for (int w = 0; w < NW; ++w) {
+      const float wt = (mw[w] == kNegInf) ? 0.f : fast_exp2((mw[w] - ms) * kLog2e);
+      l += wt * sm_l[w][h];
+      a += wt * sm_acc[w][h][d];
     }
     const size_t row = ((size_t)b * Hq + hk * G + h) * S + s;
     part_acc[row * D + d] = a;

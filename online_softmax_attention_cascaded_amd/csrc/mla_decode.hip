@@ -107,7 +107,7 @@ __device__ __forceinline__ void merge_if_last(int* __restrict__ counters, int* s
     for (int i = 0; i < 4; ++i) acc[i] = acc[i] * wa + as[i] * wb;
     m = mn;
   }
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  const float inv = (l > 0.f) ? 1.f / l : (l == 0.f ? 0.f : l);  // a NaN in l stays NaN
   const size_t orow = ((size_t)b * H + head) * DL + c0;
   if (out_bf16) {
     u32x4 w[2];
@@ -125,7 +125,7 @@ __device__ __forceinline__ void merge_if_last(int* __restrict__ counters, int* s
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = acc[i] * inv;
   }
-  if (lse && (t & 31) == 0) lse[(size_t)b * H + head] = (m == kNegInf) ? kNegInf : m + logf(l);
+  if (lse && (t & 31) == 0) lse[(size_t)b * H + head] = (m == kNegInf && l == 0.f) ? kNegInf : m + logf(l);
   if (t == 0) counters[cidx] = 0;
 }
 

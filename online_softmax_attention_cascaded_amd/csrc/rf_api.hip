@@ -1,6 +1,8 @@
-// C entry points of the library: argument validation, then one or two launches
-// on the caller's stream. Validation touches no HIP API, so every error return
-// happens before anything is enqueued (and works on a machine without a GPU).
+// C entry points of the library: argument validation, then one or more launches
+// on the caller's stream. Validation touches no HIP API, so every argument
+// error is returned before anything is enqueued (and works on a machine
+// without a GPU); only a launch the runtime refuses can leave earlier launches
+// of the same call enqueued.
 #include <stdarg.h>
 #include <stdio.h>
 

@@ -165,10 +165,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Merge of two online-softmax statistics (m, l): both rescaled to the larger max.
-// A side with m = -inf is the identity and contributes nothing.
+// A side with m = -inf is the identity and contributes nothing (weight 0; a NaN
+// in its l still reaches the result, as 0 * NaN).
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
   const float mn = fmaxf(m, m2);
-  if (mn == kNegInf) return;
   const float a = (m == kNegInf) ? 0.f : fast_exp2((m - mn) * kLog2e);
   const float b = (m2 == kNegInf) ? 0.f : fast_exp2((m2 - mn) * kLog2e);
   l = l * a + l2 * b;

@@ -193,3 +193,41 @@ def test_routing_nan_locality(E, k):
     keep[[7, 600]] = False
     assert same(w1[keep], w0[keep]) and same(i1[keep], i0[keep])
     assert ((i1[~keep] >= 0) & (i1[~keep] < E)).all()       # indices still name experts
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_mla_nan_locality(fused):
+    """A NaN in one query head spoils that head only, in both launch forms; a
+    NaN in one latent row spoils the sequence's heads and no other sequence."""
+    print_case(test="mla_nan", fused=fused)
+    B, H, Lk, S = 3, 32, 700, 5
+    q, kv = (t.to(DEV) for t in inputs.mla_inputs(42, B, H, Lk))
+    o0, l0, _ = rf.mla_decode(q, kv, 0.05, S, out_dtype=torch.float32, fused=fused)
+    q2 = q.clone()
+    q2[1, 20, 300] = NAN
+    o1, l1, _ = rf.mla_decode(q2, kv, 0.05, S, out_dtype=torch.float32, fused=fused)
+    row = torch.zeros((B, H), dtype=torch.bool, device=DEV)
+    row[1, 20] = True
+    assert nan_where(o1[row]).all() and nan_where(l1[row]).all()
+    assert same(o1[~row], o0[~row]) and same(l1[~row], l0[~row])
+    kv2 = kv.clone()
+    kv2[2, 450, 7] = NAN
+    o2, l2, _ = rf.mla_decode(q, kv2, 0.05, S, out_dtype=torch.float32, fused=fused)
+    seq = torch.zeros((B, H), dtype=torch.bool, device=DEV)
+    seq[2] = True
+    assert nan_where(o2[seq]).all() and nan_where(l2[seq]).all()
+    assert same(o2[~seq], o0[~seq]) and same(l2[~seq], l0[~seq])
+
+
+def test_merge_all_nan_state_row():
+    """A row whose only non-empty state has l = NaN (what a segment of all-NaN
+    scores leaves: max -inf, l NaN) merges to NaN, not to an empty row."""
+    print_case(test="merge_nan_state")
+    m = torch.full((2, 3), float("-inf"), device=DEV)
+    l = torch.zeros((2, 3), device=DEV)
+    acc = torch.zeros((2, 3, 128), device=DEV)
+    l[0, 1] = NAN
+    acc[0, 1] = NAN
+    o, lse = rf.merge_states(m, l, acc, out_dtype=torch.float32)
+    assert torch.isnan(o[0]).all() and torch.isnan(lse[0])
+    assert (o[1] == 0).all() and lse[1] == float("-inf")
