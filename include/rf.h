@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define RF_ABI_VERSION 7
+#define RF_ABI_VERSION 8
 
 typedef enum {
   RF_OK = 0,
@@ -256,7 +256,7 @@ rf_status rf_absmax_quant_fp8(const void* x, int rows, int cols, uint8_t* q, flo
  *   a       [M, K] bf16
  *   b       [N, K] uint8 e4m3 codes (K contiguous; the K x N operand stored
  *           column by column), b_scale [N] fp32 (per output column)
- *   a_q     [M, K] uint8 workspace, written (caller-owned, 8-byte aligned)
+ *   a_q     [M, K] uint8 workspace, written (caller-owned, 16-byte aligned)
  *   a_scale [M] fp32, written
  *   c       [M, N] bf16
  *   K % 128 == 0 and K <= 8192; M, N >= 0.
@@ -264,6 +264,27 @@ rf_status rf_absmax_quant_fp8(const void* x, int rows, int cols, uint8_t* q, flo
 rf_status rf_absmax_quant_gemm_fp8(const void* a, const uint8_t* b, const float* b_scale, int M,
                                    int N, int K, uint8_t* a_q, float* a_scale, void* c,
                                    hipStream_t stream);
+
+/*
+ * rf_absmax_quant_gemm_fp8_noalloc -- rf_absmax_quant_gemm_fp8 for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, hosts that forbid hipMalloc): the same two kernels, with the
+ * quantised A held in a library-owned device array of RF_NOALLOC_SCRATCH_BYTES
+ * (one copy per GPU, kept until the process ends) instead of a caller
+ * workspace. The call allocates nothing; its first call on a device looks up
+ * that device's copy of the array.
+ *
+ *   a, b, b_scale, a_scale, c, M, N, K as for rf_absmax_quant_gemm_fp8.
+ *   M * K <= RF_NOALLOC_SCRATCH_BYTES, else RF_ERR_UNSUPPORTED.
+ *   Every call on one GPU uses the same array: calls that can overlap on one
+ *   GPU (other streams, other host threads) race and must be serialised by the
+ *   caller. Each call writes every scratch byte it reads, so nothing has to be
+ *   cleared between calls.
+ */
+#define RF_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+rf_status rf_absmax_quant_gemm_fp8_noalloc(const void* a, const uint8_t* b, const float* b_scale,
+                                           int M, int N, int K, float* a_scale, void* c,
+                                           hipStream_t stream);
 
 /*
  * rf_absmax_quant_gemm_fp8_running -- the FP8 cascade as one pass with a running

@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     row_variance,
     rf_absmax_quant_fp8,
     rf_absmax_quant_gemm_fp8,
+    rf_absmax_quant_gemm_fp8_noalloc,
     rf_absmax_quant_gemm_fp8_running,
     rf_attn_decode_split,
     rf_attn_fwd,

@@ -38,6 +38,7 @@ SIGNATURES = {
     "rf_absmax_quant_fp8": [_P, _I, _I, _P, _P, _P],
     "rf_absmax_quant_gemm_fp8": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
     "rf_absmax_quant_gemm_fp8_running": [_P, _P, _P, _I, _I, _I, _P, _P, _P],
+    "rf_absmax_quant_gemm_fp8_noalloc": [_P, _P, _P, _I, _I, _I, _P, _P, _P],
     "rf_peak_mfma": [_I, _P, _I, _I, _P, _P, _P],
     "rf_peak_read": [_P, ctypes.c_longlong, _I, _P, _P],
     "rf_wall_clock_khz": [ctypes.POINTER(ctypes.c_int)],
@@ -303,6 +304,16 @@ def rf_absmax_quant_gemm_fp8(a, b_q, b_scale, a_q, a_scale, c):
     _dev(a, b_q, b_scale, a_q, a_scale, c)
     _check(lib().rf_absmax_quant_gemm_fp8(_ptr(a), _ptr(b_q), _ptr(b_scale), M, N, K, _ptr(a_q),
                                           _ptr(a_scale), _ptr(c), _stream(a)))
+
+
+def rf_absmax_quant_gemm_fp8_noalloc(a, b_q, b_scale, a_scale, c):
+    """The FP8 cascade with the quantised A in the library's own device scratch
+    (no workspace argument, nothing allocated)."""
+    fn = "rf_absmax_quant_gemm_fp8_noalloc"
+    M, N, K = _gemm_shapes(fn, a, b_q, b_scale, a_scale, c)
+    _dev(a, b_q, b_scale, a_scale, c)
+    _check(lib().rf_absmax_quant_gemm_fp8_noalloc(_ptr(a), _ptr(b_q), _ptr(b_scale), M, N, K,
+                                                  _ptr(a_scale), _ptr(c), _stream(a)))
 
 
 def rf_absmax_quant_gemm_fp8_running(a, b_q, b_scale, a_scale, c):

@@ -312,6 +312,33 @@ rf_status rf_absmax_quant_gemm_fp8(const void* a, const uint8_t* b, const float*
                      "rf_absmax_quant_gemm_fp8 (gemm)");
 }
 
+rf_status rf_absmax_quant_gemm_fp8_noalloc(const void* a, const uint8_t* b, const float* b_scale,
+                                           int M, int N, int K, float* a_scale, void* c,
+                                           hipStream_t stream) {
+  RF_REQUIRE(M >= 0 && N >= 0 && K >= 0, RF_ERR_INVALID_ARG, "rf_absmax_quant_gemm_fp8_noalloc: negative size");
+  if ((long long)M * N == 0) return ok();
+  RF_REQUIRE(K >= 128 && K % 128 == 0, RF_ERR_INVALID_ARG,
+             "rf_absmax_quant_gemm_fp8_noalloc: K=%d must be a positive multiple of 128", K);
+  RF_REQUIRE(K <= 8192, RF_ERR_UNSUPPORTED, "rf_absmax_quant_gemm_fp8_noalloc: K=%d > 8192", K);
+  RF_REQUIRE((long long)M * K <= (long long)rf::kNoallocScratchBytes, RF_ERR_UNSUPPORTED,
+             "rf_absmax_quant_gemm_fp8_noalloc: M*K=%lld bytes of quantised A exceed the %lld-byte "
+             "scratch (use rf_absmax_quant_gemm_fp8 with a workspace)",
+             (long long)M * K, (long long)rf::kNoallocScratchBytes);
+  RF_REQUIRE(a && b && b_scale && a_scale && c, RF_ERR_INVALID_ARG,
+             "rf_absmax_quant_gemm_fp8_noalloc: null tensor pointer");
+  RF_REQUIRE(aligned(a, 16) && aligned(b, 16) && aligned(c, 4) && aligned(b_scale, 4) &&
+                 aligned(a_scale, 4),
+             RF_ERR_INVALID_ARG, "rf_absmax_quant_gemm_fp8_noalloc: misaligned pointer");
+  void* a_q = nullptr;
+  hipError_t e = rf::noalloc_scratch(&a_q);
+  if (e != hipSuccess) return from_launch(e, "rf_absmax_quant_gemm_fp8_noalloc (scratch address)");
+  e = rf::launch_absmax_quant_fp8(a, M, K, static_cast<uint8_t*>(a_q), a_scale, stream);
+  if (e != hipSuccess) return from_launch(e, "rf_absmax_quant_gemm_fp8_noalloc (quantise)");
+  return from_launch(rf::launch_gemm_fp8_scaled(static_cast<const uint8_t*>(a_q), a_scale, b, b_scale, M,
+                                                N, K, c, stream),
+                     "rf_absmax_quant_gemm_fp8_noalloc (gemm)");
+}
+
 rf_status rf_absmax_quant_gemm_fp8_running(const void* a, const uint8_t* b, const float* b_scale,
                                            int M, int N, int K, float* a_scale, void* c,
                                            hipStream_t stream) {

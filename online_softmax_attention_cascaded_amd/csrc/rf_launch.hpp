@@ -4,9 +4,17 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/rf.h"
+
 namespace rf {
+
+// Size of the library-owned device scratch (one copy per GPU) and the lookup
+// of its device address on the current device (noalloc.hip).
+constexpr size_t kNoallocScratchBytes = RF_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** out);
 
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
                                float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int d,

@@ -55,7 +55,7 @@ def test_argument_counts_match_header():
 
 
 def test_status_helpers(lib):
-    assert lib.rf_abi_version() == 7
+    assert lib.rf_abi_version() == 8
     assert lib.rf_status_string(OK) == b"RF_OK"
     assert lib.rf_status_string(INVALID) == b"RF_ERR_INVALID_ARG"
     assert lib.rf_status_string(UNSUPPORTED) == b"RF_ERR_UNSUPPORTED"
@@ -264,6 +264,15 @@ def test_quant_validation(lib):
     assert g(FAKE, FAKE, FAKE, 64, 64, 16384, FAKE, FAKE, FAKE, None) == UNSUPPORTED
     assert g(FAKE, FAKE, FAKE, 64, 64, 256, None, FAKE, FAKE, None) == INVALID
     assert g(None, None, None, 0, 64, 256, None, None, None, None) == OK
+    n = lib.rf_absmax_quant_gemm_fp8_noalloc
+    assert n(FAKE, FAKE, FAKE, 64, 64, 100, FAKE, FAKE, None) == INVALID
+    assert n(FAKE, FAKE, FAKE, 64, 64, 16384, FAKE, FAKE, None) == UNSUPPORTED
+    assert n(FAKE, FAKE, FAKE, 64, 64, 256, None, FAKE, None) == INVALID
+    assert n(MISALIGNED, FAKE, FAKE, 64, 64, 256, FAKE, FAKE, None) == INVALID
+    # the quantised A must fit the 32 MiB scratch: 4097 x 8192 bytes does not
+    assert n(FAKE, FAKE, FAKE, 4097, 64, 8192, FAKE, FAKE, None) == UNSUPPORTED
+    assert b"scratch" in lib.rf_last_error()
+    assert n(None, None, None, 0, 64, 256, None, None, None) == OK
 
 
 def test_binding_refuses_host_tensors():

@@ -178,3 +178,11 @@ def test_gemm_checks():
     refused(g, HOST, a, bq, bs, as_, c)
     refused(g, r"rf_absmax_quant_gemm_fp8_running: a_scale has shape", a, bq, bs, z(48), c)
     refused(g, r"rf_absmax_quant_gemm_fp8_running: c has dtype", a, bq, bs, as_, z(32, 48))
+
+
+def test_gemm_noalloc_checks():
+    f = bd.rf_absmax_quant_gemm_fp8_noalloc
+    a, bq, bs, as_, c = gemm_args()
+    refused(f, HOST, a, bq, bs, as_, c)
+    refused(f, r"rf_absmax_quant_gemm_fp8_noalloc: a_scale has shape", a, bq, bs, z(48), c)
+    refused(f, r"rf_absmax_quant_gemm_fp8_noalloc: b_q has dtype", a, z(48, 256), bs, as_, c)
