@@ -60,10 +60,13 @@ typedef enum {
   RF_OK = 0,
   RF_ERR_INVALID_ARG = 1, /* null pointer, misalignment, negative size, inconsistent shape */
   RF_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for (dtype, head size, k, K) */
-  RF_ERR_LAUNCH = 3       /* the HIP runtime refused a launch; detail in rf_last_error() */
+  RF_ERR_LAUNCH = 3,      /* the HIP runtime refused a launch; detail in rf_last_error() */
+  RF_STATUS_MAX_ENUM_ = 0x7fffffff /* not a status: makes every non-negative int a valid value */
 } rf_status;
 
-typedef enum { RF_F32 = 0, RF_BF16 = 1 } rf_dtype;
+/* Element type. Any non-negative int may be passed; others than the two named
+ * here are rejected with RF_ERR_INVALID_ARG. */
+typedef enum { RF_F32 = 0, RF_BF16 = 1, RF_DTYPE_MAX_ENUM_ = 0x7fffffff } rf_dtype;
 
 /*
  * rf_attn_fwd -- O = softmax(scale * Q K^T [+ causal mask]) V, one pass over
@@ -358,6 +361,12 @@ const char* rf_last_error(void);
 
 /* RF_ABI_VERSION of the built library. */
 int rf_abi_version(void);
+
+/* Identity of the sources the library was built from: a hex digest of every
+ * kernel source and header, this header and the compiler flags, fixed at build
+ * time. A loader compares it with the digest of the sources it was shipped
+ * with and refuses a library built from others. */
+const char* rf_build_id(void);
 
 #ifdef __cplusplus
 }

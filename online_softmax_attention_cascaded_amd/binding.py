@@ -14,7 +14,7 @@ import os
 
 import torch
 
-from .build import LIB_PATH
+from .build import LIB_PATH, source_digest
 
 RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_LAUNCH = 0, 1, 2, 3
 RF_F32, RF_BF16 = 0, 1
@@ -45,8 +45,10 @@ SIGNATURES = {
     "rf_status_string": [_I],
     "rf_last_error": [],
     "rf_abi_version": [],
+    "rf_build_id": [],
 }
-_RESTYPES = {"rf_status_string": ctypes.c_char_p, "rf_last_error": ctypes.c_char_p}
+_RESTYPES = {"rf_status_string": ctypes.c_char_p, "rf_last_error": ctypes.c_char_p,
+             "rf_build_id": ctypes.c_char_p}
 
 _lib = None
 
@@ -74,6 +76,12 @@ def lib():
             fn = getattr(handle, name)
             fn.argtypes = args
             fn.restype = _RESTYPES.get(name, ctypes.c_int)
+        built, want = handle.rf_build_id().decode(), source_digest()
+        if built != want:
+            raise RuntimeError(
+                f"{LIB_PATH} was built from other sources (build id {built}, sources {want}): "
+                "rebuild it with __graft_entry__.build() or "
+                "python -m online_softmax_attention_cascaded_amd.build")
         _lib = handle
     return _lib
 

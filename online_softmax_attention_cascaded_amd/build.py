@@ -7,6 +7,7 @@ does the same from the command line.
 
 import concurrent.futures
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -14,6 +15,7 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 SRC_DIR = os.path.join(PKG_DIR, "csrc")
+HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "rf.h")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "librf.so")
 ARCH = "gfx950"
@@ -30,6 +32,21 @@ HIPCC_FLAGS = [
 ]
 
 
+def source_digest():
+    """Hash of what librf.so is built from: every csrc source and header, the
+    public header and the compiler flags. Compiled into the library as
+    rf_build_id(); the binding refuses a library whose id differs."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(SRC_DIR, "*.hip")) + glob.glob(os.path.join(SRC_DIR, "*.hpp")))
+    for f in files + [HEADER]:
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    h.update(" ".join(HIPCC_FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
 def hipcc():
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -37,9 +54,9 @@ def hipcc():
     return path
 
 
-def _compile(src):
+def _compile(src, digest):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, f'-DRF_BUILD_ID="{digest}"', "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
@@ -51,8 +68,9 @@ def build(verbose=False):
     os.makedirs(BUILD_DIR, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(SRC_DIR, "*.hip")))
     workers = min(len(sources), max(1, min(8, os.cpu_count() or 1)))
+    digest = source_digest()
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, sources))
+        objs = list(ex.map(lambda src: _compile(src, digest), sources))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

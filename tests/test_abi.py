@@ -302,3 +302,18 @@ def test_peak_validation(lib):
     assert g(FAKE, 1024, 0, FAKE, None) == INVALID
     assert g(FAKE, 1024, 4, None, None) == INVALID
     assert g(MISALIGNED, 1024, 4, FAKE, None) == INVALID
+
+
+def test_build_id_matches_the_sources(lib):
+    from online_softmax_attention_cascaded_amd.build import source_digest
+
+    assert lib.rf_build_id().decode() == source_digest()
+
+
+def test_binding_refuses_a_library_from_other_sources(monkeypatch):
+    """A librf.so whose build id differs from the digest of the sources next to
+    it (a stale build) is refused when it is loaded."""
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "source_digest", lambda: "0000000000000000")
+    with pytest.raises(RuntimeError, match="built from other sources"):
+        binding.lib()
