@@ -2,12 +2,14 @@
 
 Test infrastructure only (see the package docstring).
 
-"RedFuser episode transcript", cue 33: the first reduction is the absolute
-maximum of each token (row); the second is the GEMM over values scaled by the
-FP8 maximum over that abs-max; the abs-max enters as one multiplicative factor,
-so when it grows the running accumulator is multiplied by old/new abs-max.
-Cues 33 and 61 say the text is real-number algebra and leaves FP8 rounding
-open. Readings taken (each a plain choice the rest supports):
+"RedFuser episode transcript", cue 33. In formulas: for row i of A,
+a_i = max_k |A_ik| and s_i = a_i / 448; then C_ij = s_i t_j sum_k Aq_ik Bq_jk,
+where Aq_ik is A_ik / s_i cast to e4m3 and t_j, Bq_j are the same for row j of
+the K x N operand stored by columns. Since s_i is a single factor outside the
+sum, a one-pass loop can carry a running s_i and, whenever it increases from
+s_old to s_new, multiply the partial sum by s_old / s_new. The cue (and cue 61)
+treats these as exact real numbers and does not fix the FP8 rounding. Readings
+taken (each a plain choice the rest supports):
 
 * scale s_i = fp32(absmax_i / 448), division correctly rounded in float32;
 * code q_ik = e4m3(fp32(A_ik / s_i)), float32 division correctly rounded, then
