@@ -464,7 +464,10 @@ def main():
                  "last workgroup merges) is slower here: each workgroup's agent-scope release is an "
                  "L2 write-back, and one workgroup folds all S states of its group"),
         "traffic": traffic.get("mla_decode_split"),
-        "traffic_note": "split kernel, mean over the timed segment counts; the merge reads the partials again"}
+        "traffic_one_launch": traffic.get("mla_decode_one_launch"),
+        "traffic_note": ("split-only kernel, mean over the timed segment counts (the merge reads the partials "
+                         "again); traffic_one_launch: the single-launch form, whose merging workgroups also "
+                         "read their group's partial states")}
     del Mq, Mkv
     progress("multi-latent decode timed")
 

@@ -129,7 +129,10 @@ __device__ __forceinline__ void merge_if_last(int* __restrict__ counters, int* s
   if (t == 0) counters[cidx] = 0;
 }
 
-template <int NST>
+// MERGE: the single-launch form (the workgroup that completes its group's
+// count folds the group's states); a separate instantiation, so the split-only
+// form carries none of that code and the two are told apart in a profile.
+template <int NST, bool MERGE>
 __global__ __launch_bounds__(512, NST == 2 ? 2 : 1) void mla_decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, float* __restrict__ part_m,
     float* __restrict__ part_l, float* __restrict__ part_acc, int H, int Lk, int S, int seg_len,
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(512, NST == 2 ? 2 : 1) void mla_decode_split_kernel
       part_m[prow] = kNegInf;
       part_l[prow] = 0.f;
     }
-    if (counters)
+    if constexpr (MERGE)
       merge_if_last(counters, s_last, b * ngroups + hg, S, H, b, hg, part_m, part_l, part_acc, o, lse,
                     out_bf16);
     return;
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(512, NST == 2 ? 2 : 1) void mla_decode_split_kernel
     part_m[prow] = m_true * kLn2;
     part_l[prow] = l_run;
   }
-  if (counters)
+  if constexpr (MERGE)
     merge_if_last(counters, s_last, b * ngroups + hg, S, H, b, hg, part_m, part_l, part_acc, o, lse,
                   out_bf16);
 }
@@ -390,12 +393,17 @@ hipError_t launch_mla_decode_split(const void* q, const void* kv, float* part_m,
   }
   auto qq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(kv);
-  if ((long long)grid.x > cus)
-    hipLaunchKernelGGL(mla_decode_split_kernel<2>, grid, dim3(512), 0, stream, qq, kk, part_m, part_l,
-                       part_acc, H, Lk, S, seg_len, scale * kLog2e, counters, o, lse, out_bf16);
-  else
-    hipLaunchKernelGGL(mla_decode_split_kernel<4>, grid, dim3(512), 0, stream, qq, kk, part_m, part_l,
-                       part_acc, H, Lk, S, seg_len, scale * kLog2e, counters, o, lse, out_bf16);
+#define RF_MLA_LAUNCH(NST_, MERGE_)                                                                  \
+  hipLaunchKernelGGL((mla_decode_split_kernel<NST_, MERGE_>), grid, dim3(512), 0, stream, qq, kk,     \
+                     part_m, part_l, part_acc, H, Lk, S, seg_len, scale * kLog2e, counters, o, lse,    \
+                     out_bf16)
+  const bool two_stage = (long long)grid.x > cus;
+  if (counters) {
+    if (two_stage) RF_MLA_LAUNCH(2, true); else RF_MLA_LAUNCH(4, true);
+  } else {
+    if (two_stage) RF_MLA_LAUNCH(2, false); else RF_MLA_LAUNCH(4, false);
+  }
+#undef RF_MLA_LAUNCH
   return hipGetLastError();
 }
 
