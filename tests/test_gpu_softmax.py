@@ -8,7 +8,11 @@ a relative error of up to 3 * 2^-24 * |x_ij - m| (about 1.8e-7 |x_ij - m|);
 the exponential itself, the sum l (at most 32 sequential terms per thread, then
 a tree), the reciprocal and the product add a few ulp more. The test takes
 relative error <= 5e-6 + 2.5e-7 |x_ij - m| for every weight above 1e-30, and
-every row of the output summing to 1 within 1e-5."""
+every row of the output summing to 1 within 1e-5. That is the flat fp32 bar
+of 1e-5 for every weight within 20 of its row's max (checked separately
+below); only weights below e^-20 (2e-9) of the row's largest one get the wider
+bar, which grows because x_ij - m itself carries a rounding error of up to
+2^-24 |x_ij - m| in fp32."""
 
 import numpy as np
 import pytest
@@ -37,6 +41,8 @@ def _compare(y, x, ref):
     rel = np.where(big, err / np.where(big, ref, 1.0), 0.0)
     excess = rel - _tol(x)
     assert excess.max() <= 0, (rel.max(), np.unravel_index(excess.argmax(), excess.shape))
+    near = np.asarray(x, np.float64).max(axis=1, keepdims=True) - np.asarray(x, np.float64) <= 20
+    assert rel[near & big].max(initial=0.0) <= SOFTMAX_REL
     assert err[~big].max(initial=0.0) <= 1e-30
 
 
