@@ -8,13 +8,15 @@
 // this path serves fp32 caches, where the contract is fp32 accuracy.
 //
 // One workgroup of 4 waves per (batch, key/value head, segment) streams the
-// segment's K and V rows once for the whole GQA group. The waves take
-// interleaved 64-key chunks; in a chunk lane j owns key j for the scores (its
-// K row in 16-byte loads, the group's query rows broadcast from LDS), the
-// chunk's max and sum per head are wave reductions, and the probabilities go
-// through LDS to the product with V, where each lane owns D / 64 columns and
-// reads whole V rows. The four waves' states are merged at the end by the
-// same rule that merges segments.
+// segment's K and V rows once for the whole GQA group; the kernel is compiled
+// per group size rounded up to a power of two (GP), so its loops over heads
+// are exact. The waves take interleaved 64-key chunks; in a chunk lane j owns
+// key j for the scores (its K row in 16-byte loads, all issued before the
+// FMAs that use them; the query rows are wave-uniform), the chunk's max and
+// sum per head are wave reductions, and the probabilities go through LDS to
+// the product with V, where each lane owns D / 64 columns of V rows read
+// eight keys ahead (four probabilities per LDS read). The four waves' states
+// are merged at the end by the same rule that merges segments.
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
 
@@ -25,13 +27,13 @@ constexpr int NW = 4;        // waves per workgroup
 constexpr int CH = 64;       // keys per chunk (one per lane)
 constexpr int MAXG = 16;     // query heads per key/value head
 
-template <int D>
+template <int D, int GP>
 __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_acc, int Hq,
     int Hkv, int Lk, int S, int seg_len, float scale) {
   constexpr int NC = D / 64;  // output columns per lane
-  __shared__ float qs[MAXG][D];
+  __shared__ float qs[MAXG][D];  // used for 8 or 16 heads only
   __shared__ float ps[NW][MAXG][CH];
   __shared__ float sm_m[NW][MAXG], sm_l[NW][MAXG];
   __shared__ float sm_acc[NW][MAXG][D];
@@ -45,18 +47,25 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
   const int t0 = min(s * seg_len, Lk), t1 = min(t0 + seg_len, Lk);
   const int nchunks = (t1 - t0 + CH - 1) / CH;
 
-  for (int i = tid; i < MAXG * D; i += 256) {
-    const int h = i / D, d = i - h * D;
-    qs[h][d] = (h < G) ? q[((size_t)b * Hq + hk * G + h) * D + d] : 0.f;
+
+  // The group's query rows: read straight from memory at wave-uniform
+  // addresses (scalar loads, FMA operands from SGPRs) for up to 4 heads; from
+  // LDS for 8 or 16 heads, whose rows do not fit the scalar registers.
+  const float* const qg = q + ((size_t)b * Hq + hk * G) * D;
+  if constexpr (GP >= 8) {
+    for (int i = tid; i < GP * D; i += 256) {
+      const int h = i / D, d = i - h * D;
+      qs[h][d] = (h < G) ? qg[h * D + d] : 0.f;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (size_t)bhk * Lk * D, (uint32_t)Lk * D * 4);
-  const float* vp = v + (size_t)bhk * Lk * D;
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (size_t)bhk * Lk * D, (uint32_t)Lk * D * 4);
+  constexpr int PVU = 8;
 
-  float m_run[MAXG], l_run[MAXG], acc[MAXG][NC];
+  float m_run[GP], l_run[GP], acc[GP][NC];
 #pragma unroll
-  for (int h = 0; h < MAXG; ++h) {
+  for (int h = 0; h < GP; ++h) {
     m_run[h] = kNegInf;
     l_run[h] = 0.f;
 #pragma unroll
@@ -68,17 +77,18 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     const int key = kbase + lane;
     const bool valid = key < t1;
     // ---- scores of key `key` against the group's query rows
-    float sc[MAXG];
+    float sc[GP];
 #pragma unroll
-    for (int h = 0; h < MAXG; ++h) sc[h] = 0.f;
-#pragma unroll 4
+    for (int h = 0; h < GP; ++h) sc[h] = 0.f;
+#pragma unroll
     for (int d4 = 0; d4 < D / 4; ++d4) {
-      const u32x4 w = buf_load16(krs, key * D * 4 + 16 * d4, 0);
+      const u32x4 w = buf_load16(krs, (int)((uint32_t)key * (D * 4) + 16 * d4), 0);
       const f32x4 kv = __builtin_bit_cast(f32x4, w);
 #pragma unroll
-      for (int h = 0; h < MAXG; ++h) {
+      for (int h = 0; h < GP; ++h) {
         if (h < G) {
-          const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[h][4 * d4]);
+          const f32x4 qv = (GP >= 8) ? *reinterpret_cast<const f32x4*>(&qs[h][4 * d4])
+                                     : *reinterpret_cast<const f32x4*>(qg + h * D + 4 * d4);
           sc[h] = fmaf(qv[0], kv[0], sc[h]);
           sc[h] = fmaf(qv[1], kv[1], sc[h]);
           sc[h] = fmaf(qv[2], kv[2], sc[h]);
@@ -88,7 +98,7 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     }
     // ---- online update per head
 #pragma unroll
-    for (int h = 0; h < MAXG; ++h) {
+    for (int h = 0; h < GP; ++h) {
       if (h < G) {
         const float x = valid ? sc[h] * scale : kNegInf;
         const float m_new = fmaxf(m_run[h], wave_max(x));
@@ -105,17 +115,31 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     __builtin_amdgcn_wave_barrier();  // the wave's own p row is read back by every lane
     // ---- acc += P V: lane owns columns cc * 64 + lane
     const int nk = min(CH, t1 - kbase);
-    for (int j = 0; j < nk; ++j) {
-      const float* vrow = vp + (size_t)(kbase + j) * D;
-      float vv[NC];
+    // eight keys' V values in flight at a time; keys past the segment are
+    // skipped (their weight is 0, and 0 * v must not touch v)
+    for (int j0 = 0; j0 < nk; j0 += PVU) {
+      float vv[PVU][NC];
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) vv[cc] = vrow[cc * 64 + lane];
+      for (int u = 0; u < PVU; ++u)
 #pragma unroll
-      for (int h = 0; h < MAXG; ++h) {
+        for (int cc = 0; cc < NC; ++cc)
+          vv[u][cc] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+              vrs, (int)(((uint32_t)(kbase + j0 + u) * D + cc * 64 + lane) * 4u), 0, 0));
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
         if (h < G) {
-          const float p = ps[wave][h][j];
 #pragma unroll
-          for (int cc = 0; cc < NC; ++cc) acc[h][cc] = fmaf(p, vv[cc], acc[h][cc]);
+          for (int u4 = 0; u4 < PVU / 4; ++u4) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&ps[wave][h][j0 + 4 * u4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int u = 4 * u4 + e;
+              if (j0 + u < nk) {
+#pragma unroll
+                for (int cc = 0; cc < NC; ++cc) acc[h][cc] = fmaf(p4[e], vv[u][cc], acc[h][cc]);
+              }
+            }
+          }
         }
       }
     }
@@ -124,7 +148,7 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
 
   // ---- merge the four waves' states (the rule that merges segments)
 #pragma unroll
-  for (int h = 0; h < MAXG; ++h) {
+  for (int h = 0; h < GP; ++h) {
     if (h < G) {
       if (lane == 0) {
         sm_m[wave][h] = m_run[h];
@@ -168,13 +192,25 @@ hipError_t launch_decode_split_f32(const float* q, const float* k, const float* 
                                    int d, int S, float scale, hipStream_t stream) {
   const int seg_len = (Lk + S - 1) / S;
   dim3 grid(B * Hkv * S);
-  if (d == 64)
-    hipLaunchKernelGGL((decode_split_f32_kernel<64>), grid, dim3(256), 0, stream, q, k, v, part_m,
-                       part_l, part_acc, Hq, Hkv, Lk, S, seg_len, scale);
-  else
-    hipLaunchKernelGGL((decode_split_f32_kernel<128>), grid, dim3(256), 0, stream, q, k, v, part_m,
-                       part_l, part_acc, Hq, Hkv, Lk, S, seg_len, scale);
+  const int G = Hq / Hkv;
+#define RF_DEC32(D_, GP_)                                                                           \
+  hipLaunchKernelGGL((decode_split_f32_kernel<D_, GP_>), grid, dim3(256), 0, stream, q, k, v, part_m, \
+                     part_l, part_acc, Hq, Hkv, Lk, S, seg_len, scale)
+#define RF_DEC32_G(D_)                    \
+  if (G <= 1) RF_DEC32(D_, 1);            \
+  else if (G <= 2) RF_DEC32(D_, 2);       \
+  else if (G <= 4) RF_DEC32(D_, 4);       \
+  else if (G <= 8) RF_DEC32(D_, 8);       \
+  else RF_DEC32(D_, 16)
+  if (d == 64) {
+    RF_DEC32_G(64);
+  } else {
+    RF_DEC32_G(128);
+  }
+#undef RF_DEC32_G
+#undef RF_DEC32
   return hipGetLastError();
 }
 
 }  // namespace rf
+
