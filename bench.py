@@ -471,6 +471,56 @@ def main():
     del Mq, Mkv
     progress("multi-latent decode timed")
 
+    # The other widths and dtypes the boundary takes, on the decode and prefill
+    # shapes: split-KV decode (split + merge) with fp32 K/V at head size 128
+    # and 64 and with bf16 K/V at head size 64, and bf16 prefill at head size 64.
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / args.steps
+
+    variants = {}
+    for name, d_, dt_ in (("decode_f32_d128", 128, torch.float32), ("decode_f32_d64", 64, torch.float32),
+                          ("decode_bf16_d64", 64, torch.bfloat16)):
+        vq, vk, vv = (t.to(dev) for t in inputs.decode_inputs(2, Dc["B"], Dc["Hq"], Dc["Hkv"], Dc["Lk"], d_,
+                                                                dtype=dt_))
+        es = 4 if dt_ == torch.float32 else 2
+        nbytes = 2 * Dc["B"] * Dc["Hkv"] * Dc["Lk"] * d_ * es + 2 * Dc["B"] * Dc["Hq"] * d_ * es
+        vo = torch.empty((Dc["B"], Dc["Hq"], d_), dtype=dt_, device=dev)
+        vl = torch.empty((Dc["B"], Dc["Hq"]), device=dev)
+        by = {}
+        for S in (4, 8, 16):
+            pm = torch.empty((Dc["B"], Dc["Hq"], S), device=dev)
+            pl = torch.empty_like(pm)
+            pa = torch.empty((Dc["B"], Dc["Hq"], S, d_), device=dev)
+
+            def dec():
+                rf.rf_attn_decode_split(vq, vk, vv, pm, pl, pa, 1 / math.sqrt(d_))
+                rf.rf_merge_states(pm, pl, pa, vo, vl)
+            by[str(S)] = round(nbytes / timed(dec) / 1e9, 1)
+        best = max(by, key=by.get)
+        variants[name] = {"bound": "hbm", "segments": int(best), "achieved": by[best], "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": round(by[best] / PEAK_HBM_GBS, 4), "by_segments": by}
+        del vq, vk, vv
+    pq, pk, pv = (t.to(dev) for t in inputs.attention_inputs(1, P["B"], P["H"], P["H"], P["L"], P["L"], 64))
+    po = torch.empty_like(pq)
+    pls = torch.empty(pq.shape[:3], dtype=torch.float32, device=dev)
+    for causal in (False, True):
+        t = timed(lambda: rf.rf_attn_fwd(pq, pk, pv, po, pls, 0.125, causal))
+        pairs = P["L"] * (P["L"] + 1) // 2 if causal else P["L"] * P["L"]
+        fl = 4.0 * P["B"] * P["H"] * pairs * 64
+        variants["prefill_d64" + ("_causal" if causal else "")] = {
+            "bound": "mfma", "achieved": round(fl / t / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4), "us_per_launch": round(t * 1e6, 2)}
+    del pq, pk, pv, po
+    result["other_widths"] = variants
+    progress("other head sizes and fp32 decode timed")
+
     # Safe softmax alone at each fusion level of the reduction tree, rows of
     # 1K .. 8K fp32 values, 2^26 values per launch (launches rotate over three
     # copies of the input, 268 MB each). The rate is counted with the

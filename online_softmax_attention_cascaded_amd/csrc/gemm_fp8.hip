@@ -142,7 +142,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const uint8_t* __
     // have, and everyone is done with stage kt-1, whose slot takes stage kt+1.
     wait_stage(0);
     lds_barrier();
-    if (kt + 1 < nk) issue(kt + 1);
     const char* st = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -153,6 +152,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const uint8_t* __
         a[0][h] = rd(st, ao[q][0][h]);
         b1[h] = rd(st, bo[q][1][h]);
         a[1][h] = rd(st, ao[q][1][h]);
+      }
+      // the next stage's loads go out behind the first fragment reads, so
+      // those reads do not queue behind them (1 % in A/B, identical output)
+      if (q == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nk) issue(kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
