@@ -3,12 +3,15 @@ configuration the bench times, compared element by element with the fp64
 oracle (the oracle finishes each workload in seconds to tens of seconds on the
 host). Bars:
 
-* prefill (B=4, H=32, L=2048, d=128, bf16): every (batch, head) slice within
-  2e-2 max absolute error and 1e-2 relative Frobenius error on O, 1e-3 on lse;
+* prefill (B=4, H=32, L=2048, d=128 and 64, bf16): every (batch, head) slice
+  within 2e-2 max absolute error and 1e-2 relative Frobenius error on O, 1e-3
+  on lse;
 * decode (B=8, Hq=32, Hkv=8, Lk=32768, d=128, bf16): every partial state of
   every row at every segment count -- m to 1e-5 relative, l to 1e-5 relative
   per element, acc to 1e-4 of its row's largest entry -- and every merged row
   (bf16 output as timed, and fp32 output to 1e-4 of the row's largest entry);
+  the same shape with fp32 K/V (d=128, 64; every state and row to 1e-5) and
+  bf16 K/V at d=64;
 * multi-latent decode (32 sequences, 16 heads, 8192 latent rows): every row
   of both launch forms at every timed segment count, as decode;
 * FP8 (M=N=4096, K=7168): every code and scale of A and B bit-exact, and every
@@ -70,6 +73,51 @@ def test_prefill_every_slice(prefill, causal):
             worst = [max(worst[0], err), max(worst[1], fro), max(worst[2], lerr)]
     print(f"128 slices in {time.time() - t:.1f} s: max abs {worst[0]:.2e}, rel fro {worst[1]:.2e}, "
           f"lse {worst[2]:.2e}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_head64_every_slice(causal):
+    """The head-size-64 prefill the bench times (B=4, H=32, L=2048), every slice."""
+    print_case(test="prefill64_full", causal=causal)
+    B, H, L, d = 4, 32, 2048, 64
+    q, k, v = inputs.attention_inputs(1, B, H, H, L, L, d)
+    scale = 0.125
+    o, lse = rf.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal=causal)
+    o, lse = np32(o), np32(lse)
+    for b in range(B):
+        for h in range(H):
+            o_ref, lse_ref = oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1],
+                                              v[b:b + 1, h:h + 1], scale, causal=causal)
+            err = np.abs(o[b, h] - o_ref[0, 0]).max()
+            fro = rel_fro(o[b, h], o_ref[0, 0])
+            lerr = np.abs(lse[b, h] - lse_ref[0, 0]).max()
+            assert err <= BF16_ABS and fro <= BF16_REL_FRO and lerr <= LSE_ABS, (b, h, err, fro, lerr)
+
+
+@pytest.mark.parametrize("d,dtype", [(128, torch.float32), (64, torch.float32), (64, torch.bfloat16)])
+def test_decode_other_widths_every_row(d, dtype):
+    """The decode shape (B=8, Hq=32, Hkv=8, Lk=32768) at the other widths and
+    dtypes the bench times, S in {4, 8, 16}: every partial state and merged row
+    (fp32 output). fp32 K/V: states and output to 1e-5 of each row's largest
+    entry (the fp32 bar); bf16 K/V: as the bf16 decode."""
+    print_case(test="decode_widths_full", d=d, dtype=dtype)
+    B, Hq, Hkv, Lk = 8, 32, 8, 32768
+    q, k, v = inputs.decode_inputs(2, B, Hq, Hkv, Lk, d, dtype=dtype)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    q64, k64, v64 = (t.to(torch.float64).numpy() for t in (q, k, v))
+    scale = 1 / math.sqrt(d)
+    o_ref, lse_ref = oracle.attention(q64[:, :, None], k64, v64, scale)
+    o_ref, lse_ref = o_ref[:, :, 0], lse_ref[:, :, 0]
+    acc_bar = 1e-5 if dtype == torch.float32 else 1e-4
+    for S in (4, 8, 16):
+        o, lse, (m, l, acc) = rf.attn_decode(qd, kd, vd, scale, S, out_dtype=torch.float32)
+        m_ref, l_ref, accr = oracle.decode_partials(q64, k64, v64, scale, S)
+        m, l, acc = np32(m), np32(l), np32(acc)
+        assert (np.abs(m - m_ref) / np.maximum(1, np.abs(m_ref))).max() <= 1e-5
+        assert (np.abs(l - l_ref) / l_ref).max() <= 1e-5
+        assert _row_normwise(acc, accr).max() <= acc_bar
+        assert _row_normwise(np32(o), o_ref).max() <= acc_bar
+        assert np.abs(np32(lse) - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
 
 
 # ------------------------------------------------------------------- decode
