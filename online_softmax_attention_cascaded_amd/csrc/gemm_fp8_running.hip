@@ -26,7 +26,8 @@
 // max), combined over the row's 4 lanes by DPP; on growth the new scale, the
 // ratio s_old / s_new (published in LDS for the step's MFMA waves) and 1 / s;
 // codes as the correctly rounded x / s (one Markstein correction of
-// x * RN(1/s)) through the hardware round-to-nearest-even e4m3 convert.
+// x * RN(1/s), exact for s >= 2^-90; smaller nonzero scales divide) through
+// the hardware round-to-nearest-even e4m3 convert.
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
 
@@ -42,6 +43,9 @@ constexpr int kOffRatio = kOffCodes + 2 * kCodes;
 constexpr int kOffScale = kOffRatio + 2 * BM * 4;
 constexpr int kSmem = kOffScale + BM * 4;    // 145.5 KB
 constexpr int kGroupM = 8;                   // tile rows per band of the tile order
+// Smallest scale of the one-correction division: below it x - s q can
+// underflow and the correction is no longer exact.
+constexpr float kMinFastScale = 0x1p-90f;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_running_kernel(
         y[2 * e] = bf16_lo(xv[e]);
         y[2 * e + 1] = bf16_hi(xv[e]);
       }
-      if (rcp <= 3.4e38f) {
+      if (!(s_run > 0.f && s_run < kMinFastScale)) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float q0 = y[j] * rcp;

@@ -7,12 +7,15 @@
 // values the bit pattern orders like the value). The scale is
 // s = fp32(absmax / 448) and every code is e4m3(fp32(x / s)) with the
 // quotient correctly rounded: r = RN(1/s) once per row, then q = RN(x r),
-// e = x - s q (exact, by fma) and RN(q + e r), which is the correctly rounded
-// x / s whenever r is the correctly rounded reciprocal (Markstein's theorem for
-// division by a reciprocal with one correction step). |x / s| <= 448 (1 + 2^-23)
-// so nothing overflows; underflow can only touch quotients far below the
-// smallest e4m3 step, whose code is 0 either way. A row so small that 1/s
-// overflows takes plain division instead. The e4m3 cast is the hardware
+// e = x - s q (by fma) and RN(q + e r), which is the correctly rounded x / s
+// whenever r is the correctly rounded reciprocal and e is exact (Markstein's
+// theorem for division by a reciprocal with one correction step). e is exact
+// when s >= 2^-90 and |q| >= 2^-12: s q is then a multiple of 2^-148 and e,
+// about 2^-23 |s q|, fits in 24 bits; smaller quotients encode to 0 whatever
+// their last bits. |x / s| <= 448 (1 + 2^-23), so nothing overflows. Rows with
+// 0 < s < 2^-90 (abs-max below about 3.6e-25) take plain division: there e can
+// underflow, and one correction step gave wrong codes (2 of about 1100 bf16
+// patterns at abs-max 2e-36, where s is subnormal). The e4m3 cast is the hardware
 // round-to-nearest-even conversion (v_cvt_pk_fp8_f32); |x / s| stays below 464,
 // so no value reaches the range where saturation would matter.
 #include "rf_device.hpp"
@@ -20,6 +23,8 @@
 
 namespace rf {
 namespace {
+
+constexpr float kMinFastScale = 0x1p-90f;  // smallest scale of the one-correction division
 
 template <int NC>  // 16-byte chunks (8 values) per lane
 __global__ __launch_bounds__(256) void absmax_quant_kernel(const uint16_t* __restrict__ x,
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(256) void absmax_quant_kernel(const uint16_t* __res
       y[2 * e] = bf16_lo(ch[c][e]);
       y[2 * e + 1] = bf16_hi(ch[c][e]);
     }
-    if (rcp <= 3.4e38f) {
+    if (!(sc > 0.f && sc < kMinFastScale)) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float q0 = y[j] * rcp;

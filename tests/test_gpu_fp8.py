@@ -65,9 +65,12 @@ def _all_bf16_rows(amax_values, seed):
 
 def test_quantiser_every_bf16_pattern():
     """The division x / s and the e4m3 rounding on every input bit pattern a row can
-    hold, for 12 row maxima (one so small that 1/s overflows fp32)."""
+    hold, for 16 row maxima: one so small that 1/s overflows fp32, two whose scale
+    is an fp32 subnormal with a finite reciprocal (there x - s q underflows and one
+    correction step of x * (1/s) is not always the correctly rounded quotient),
+    and two around 448 * 2^-90, the smallest scale the fast path takes."""
     x = _all_bf16_rows([448.0, 1.0, 3.5, 0.0078125, 1e-3, 17.25, 6.0e4, 2.0 ** -100, 123.456, 0.3,
-                        1e30, 5e-38], seed=13)
+                        1e30, 5e-38, 2e-36, 4e-36, 1e-25, 1e-24], seed=13)
     print_case(test="quant_all_bf16", rows=x.shape[0])
     q, s = rf.absmax_quant_fp8(x.to(DEV))
     q_ref, s_ref = oracle.absmax_quant(x.float().numpy())
@@ -115,6 +118,27 @@ def test_running_scale_gemm_small(M, N, K):
     c, c_ref, sa, sa_ref, _, _ = _running_case(a, bsrc)
     assert np.array_equal(sa, sa_ref)          # the final running scale is the row's scale
     assert rel_fro(c, c_ref) <= 5e-3
+
+
+def test_running_scale_tiny_scales():
+    """Rows with tiny scales: fp32 subnormal scales whose reciprocal overflows and
+    ones whose reciprocal is finite, normal scales below 2^-90, a row that grows
+    from tiny to normal size and one that shrinks. The divisions of those rows do
+    not take the one-correction path, and the result still matches the
+    oracle."""
+    M, N, K = 64, 128, 1024
+    a, bsrc = inputs.quant_inputs(14, M, N, K)
+    a = a.clone()
+    a[0:8] *= 1e-37      # abs-max ~4e-37: s ~1e-39, 1/s overflows
+    a[8:16] *= 1e-36     # abs-max ~4e-36: s ~1e-38 (subnormal), 1/s finite
+    a[16:24] *= 1e-26    # s ~1e-28: normal, below 2^-90
+    a[24, :512] *= 1e-36
+    a[25, 512:] *= 1e-36
+    print_case(test="gemm_running_tiny")
+    c, c_ref, sa, sa_ref, _, _ = _running_case(a, bsrc)
+    assert np.array_equal(sa, sa_ref)
+    for r in range(M):
+        assert rel_fro(c[r], c_ref[r]) <= 5e-3, r
 
 
 def test_running_scale_growth_and_zero_rows():
