@@ -98,7 +98,8 @@ rf_status rf_attn_fwd(rf_dtype dt, const void* q, const void* k, const void* v, 
  *
  *   dt     RF_BF16: q [B, Hq, d], k, v [B, Hkv, Lk, d] bf16, scores and
  *          P V on MFMA with fp32 accumulation; RF_F32: q, k, v fp32, all
- *          arithmetic fp32 (FMA).
+ *          arithmetic fp32 (fp32 MFMA v_mfma_f32_16x16x4_f32: fp32 products
+ *          and sums).
  *   d in {64, 128}; Hq % Hkv == 0 and Hq / Hkv <= 16; S >= 1; Lk >= 1; one
  *   head's K (or V) under 2 GiB (Lk * d * sizeof(element) < 2^31, else
  *   RF_ERR_UNSUPPORTED).
