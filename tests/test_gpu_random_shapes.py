@@ -1,0 +1,185 @@
+"""Seeded random shapes for every entry point of the path, compared with the
+fp64 oracle at the bars the per-kernel tests use. The per-kernel tests pick
+their shapes by hand (one tile, ragged tails, empty segments, the configs);
+these draw the sizes at random within what each entry point accepts (GQA
+groups 1-16, head sizes 64 and 128, 1-69 segments, rows of any multiple of 4
+or 8 values up to the limits, GEMM sides of any length and K any multiple of
+128), so that combinations nobody picked meet the kernels too. The draws are
+fixed by the seed below, so every run tests the same cases."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import online_softmax_attention_cascaded_amd as rf
+from online_softmax_attention_cascaded_amd import inputs
+from gpu_util import (DEV, FP32_REL, assert_bf16_attention, needs_gpu, normwise, np32,
+                      print_case, rel_fro)
+from test_gpu_decode import _check_partials
+from test_gpu_moments import _compare as _compare_moments
+from test_gpu_softmax import _compare as _compare_softmax
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+_rng = np.random.default_rng(20261202)
+
+
+def _draw(n, fn):
+    return [fn(_rng) for _ in range(n)]
+
+
+def _attn_case(r):
+    d = int(r.choice([64, 128]))
+    Hkv = int(r.integers(1, 4))
+    G = int(r.choice([1, 2, 3, 4, 8]))
+    causal = bool(r.integers(0, 2))
+    Lk = int(r.integers(1, 400))
+    Lq = Lk if causal else int(r.integers(1, 400))
+    return (int(r.integers(1, 3)), Hkv * G, Hkv, Lq, Lk, d, causal)
+
+
+def _decode_case(r):
+    d = int(r.choice([64, 128]))
+    Hkv = int(r.integers(1, 4))
+    G = int(r.integers(1, 17))
+    Lk = int(r.integers(1, 3000))
+    S = int(r.integers(1, 70))
+    return (int(r.integers(1, 3)), Hkv * G, Hkv, Lk, d, S)
+
+
+ATTN_BF16 = _draw(30, _attn_case)
+ATTN_F32 = _draw(12, _attn_case)
+DECODE_BF16 = _draw(30, _decode_case)
+DECODE_F32 = _draw(20, _decode_case)
+ROUTING = _draw(30, lambda r: (int(r.integers(1, 200)), int(4 * r.integers(1, 257)), int(r.integers(1, 33)),
+                               bool(r.integers(0, 2))))
+QUANT = _draw(20, lambda r: (int(r.integers(1, 40)), int(8 * r.integers(1, 1025))))
+GEMM = _draw(20, lambda r: (int(r.integers(1, 300)), int(r.integers(1, 300)), int(128 * r.integers(1, 17))))
+MLA = _draw(12, lambda r: (int(r.integers(1, 4)), int(r.choice([16, 32])), int(r.integers(1, 1500)),
+                          int(r.integers(1, 13)), bool(r.integers(0, 2))))
+ROWS = _draw(30, lambda r: (int(r.integers(1, 40)), int(4 * r.integers(1, 2049)), int(r.integers(0, 4))))
+
+
+@pytest.mark.parametrize("case", ATTN_BF16, ids=str)
+def test_random_attention_bf16(case):
+    B, Hq, Hkv, Lq, Lk, d, causal = case
+    print_case(test="random_attn_bf16", shape=case)
+    q, k, v = inputs.attention_inputs(31, B, Hq, Hkv, Lq, Lk, d)
+    scale = 1 / math.sqrt(d)
+    o, lse = rf.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal=causal)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal)
+    assert_bf16_attention(np32(o), o_ref, np32(lse), lse_ref, what=str(case))
+
+
+@pytest.mark.parametrize("case", ATTN_F32, ids=str)
+def test_random_attention_fp32(case):
+    B, Hq, Hkv, Lq, Lk, d, causal = case
+    print_case(test="random_attn_fp32", shape=case)
+    q, k, v = inputs.attention_inputs(32, B, Hq, Hkv, Lq, Lk, d, dtype=torch.float32)
+    scale = 1 / math.sqrt(d)
+    o, lse = rf.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal=causal)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal)
+    assert normwise(np32(o), o_ref) <= FP32_REL
+    assert np.abs(np32(lse) - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+
+
+def _decode(case, dtype, seed, acc_bar, out_bar):
+    B, Hq, Hkv, Lk, d, S = case
+    q, k, v = inputs.decode_inputs(seed, B, Hq, Hkv, Lk, d, dtype=dtype)
+    scale = 1 / math.sqrt(d)
+    o, lse, (m, l, acc) = rf.attn_decode(q.to(DEV), k.to(DEV), v.to(DEV), scale, S, out_dtype=torch.float32)
+    _check_partials(m, l, acc, *oracle.decode_partials(q, k, v, scale, S), acc_bar=acc_bar)
+    o_ref, lse_ref = oracle.attention(q[:, :, None], k, v, scale)
+    assert normwise(np32(o), o_ref[:, :, 0]) <= out_bar
+    assert np.abs(np32(lse) - lse_ref[:, :, 0]).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+
+
+@pytest.mark.parametrize("case", DECODE_BF16, ids=str)
+def test_random_decode_bf16(case):
+    print_case(test="random_decode_bf16", shape=case)
+    _decode(case, torch.bfloat16, 33, 1e-4, 1e-4)
+
+
+@pytest.mark.parametrize("case", DECODE_F32, ids=str)
+def test_random_decode_fp32(case):
+    print_case(test="random_decode_fp32", shape=case)
+    _decode(case, torch.float32, 34, FP32_REL, FP32_REL)
+
+
+@pytest.mark.parametrize("case", ROUTING, ids=str)
+def test_random_routing(case):
+    T, E, k, renorm = case
+    k = min(k, E)
+    print_case(test="random_routing", T=T, E=E, k=k, renormalize=renorm)
+    x = inputs.routing_inputs(35, T, E)
+    w, idx = rf.softmax_topk(x.to(DEV), k, renorm)
+    w_ref, idx_ref = oracle.softmax_topk(x.numpy(), k, renorm)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert (np.abs(np32(w) - w_ref) / w_ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("case", QUANT, ids=str)
+def test_random_quantiser(case):
+    rows, cols = case
+    print_case(test="random_quant", rows=rows, cols=cols)
+    x, _ = inputs.quant_inputs(36, rows, 1, cols)
+    q, s = rf.absmax_quant_fp8(x.to(DEV))
+    q_ref, s_ref = oracle.absmax_quant(x.float().numpy())
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("case", GEMM, ids=str)
+def test_random_fp8_gemms(case):
+    """The two-pass cascade (codes, scales and C) and the one-pass running-scale
+    form (final scales and C) on the same operands."""
+    M, N, K = case
+    print_case(test="random_fp8", M=M, N=N, K=K)
+    a, bsrc = inputs.quant_inputs(37, M, N, K)
+    bq, bs = rf.absmax_quant_fp8(bsrc.to(DEV))
+    c, aq, sa = rf.absmax_quant_gemm_fp8(a.to(DEV), bq, bs)
+    aq_ref, sa_ref = oracle.absmax_quant(a.float().numpy())
+    assert np.array_equal(sa.cpu().numpy(), sa_ref)
+    assert np.array_equal(aq.cpu().numpy(), aq_ref)
+    c_ref = oracle.quant_gemm(aq_ref, sa_ref, bq.cpu().numpy(), bs.cpu().numpy())
+    assert rel_fro(np32(c), c_ref) <= 5e-3
+    c2, sa2 = rf.absmax_quant_gemm_fp8_running(a.to(DEV), bq, bs)
+    c2_ref = oracle.quant_gemm_running_scale(a.float().numpy(), bq.cpu().numpy(), bs.cpu().numpy(), 64)
+    assert np.array_equal(sa2.cpu().numpy(), sa_ref)
+    assert rel_fro(np32(c2), c2_ref) <= 5e-3
+
+
+@pytest.mark.parametrize("case", MLA, ids=str)
+def test_random_mla(case):
+    B, H, Lk, S, fused = case
+    print_case(test="random_mla", B=B, H=H, Lk=Lk, S=S, fused=fused)
+    q, kv = inputs.mla_inputs(38, B, H, Lk)
+    scale = 1 / math.sqrt(576)
+    o, lse, _ = rf.mla_decode(q.to(DEV), kv.to(DEV), scale, S, out_dtype=torch.float32, fused=fused)
+    lat = kv[:, None]
+    o_ref, lse_ref = oracle.attention(q[:, :, None], lat, lat[..., :512], scale)
+    o_ref, lse_ref = o_ref[:, :, 0], lse_ref[:, :, 0]
+    assert (np.abs(np32(o) - o_ref).max(-1) / np.abs(o_ref).max(-1)).max() <= 1e-4
+    assert np.abs(np32(lse) - lse_ref).max() <= 1e-5 * np.abs(lse_ref).max()
+
+
+@pytest.mark.parametrize("case", ROWS, ids=str)
+def test_random_row_cascades(case):
+    """Softmax, variance and inertia of the same row sizes at one fusion level."""
+    T, E, level = case
+    print_case(test="random_rows", T=T, E=E, level=level)
+    x = inputs.softmax_inputs(39, T, E)
+    y = rf.softmax(x.to(DEV), level).cpu().numpy().astype(np.float64)
+    _compare_softmax(y, x.numpy(), oracle.softmax_rows(x.numpy()))
+    xm, w = inputs.moment_inputs(40, T, E)
+    mean, var = rf.row_variance(xm.to(DEV), level)
+    m_ref, v_ref = oracle.row_variance(xm.numpy())
+    _compare_moments(mean.cpu().numpy(), var.cpu().numpy() * E, m_ref, v_ref * E, np.full(T, float(E)),
+                     f"{case} variance")
+    centre, inertia = rf.row_inertia(xm.to(DEV), w.to(DEV), level)
+    c_ref, i_ref = oracle.row_inertia(xm.numpy(), w.numpy())
+    _compare_moments(centre.cpu().numpy(), inertia.cpu().numpy(), c_ref, i_ref, w.numpy().astype(np.float64).sum(1),
+                     f"{case} inertia")
