@@ -183,3 +183,49 @@ def test_random_row_cascades(case):
     c_ref, i_ref = oracle.row_inertia(xm.numpy(), w.numpy())
     _compare_moments(centre.cpu().numpy(), inertia.cpu().numpy(), c_ref, i_ref, w.numpy().astype(np.float64).sum(1),
                      f"{case} inertia")
+
+
+# ---- large logits: scores of standard deviation sigma^2 (one-hot softmax rows,
+# the reference of every row moving many times along the key axis)
+
+@pytest.mark.parametrize("sigma", [4.0, 8.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_logits_attention(sigma, causal):
+    B, Hq, Hkv, L, d = 1, 4, 2, 333, 128
+    print_case(test="large_logits_attn", sigma=sigma, causal=causal)
+    q, k, v = inputs.attention_inputs(41, B, Hq, Hkv, L, L, d)
+    q = (q.float() * sigma).to(torch.bfloat16)
+    k = (k.float() * sigma).to(torch.bfloat16)
+    scale = 1 / math.sqrt(d)
+    o, lse = rf.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal=causal)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal)
+    assert_bf16_attention(np32(o), o_ref, np32(lse), lse_ref, what=f"sigma={sigma}")
+
+
+@pytest.mark.parametrize("sigma", [4.0, 8.0])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_large_logits_decode(sigma, dtype):
+    B, Hq, Hkv, Lk, d, S = 2, 8, 2, 2500, 128, 7
+    print_case(test="large_logits_decode", sigma=sigma, dtype=dtype)
+    q, k, v = inputs.decode_inputs(42, B, Hq, Hkv, Lk, d, dtype=dtype)
+    q = (q.float() * sigma).to(dtype)
+    k = (k.float() * sigma).to(dtype)
+    scale = 1 / math.sqrt(d)
+    o, lse, (m, l, acc) = rf.attn_decode(q.to(DEV), k.to(DEV), v.to(DEV), scale, S, out_dtype=torch.float32)
+    bar = 1e-4 if dtype == torch.bfloat16 else FP32_REL
+    m_ref, l_ref, acc_ref = oracle.decode_partials(q, k, v, scale, S)
+    m, l, acc = (np.asarray(np32(t), np.float64) for t in (m, l, acc))
+    assert np.array_equal(np.isinf(m), np.isinf(m_ref))
+    fin = ~np.isinf(m_ref)
+    assert np.abs(m[fin] - m_ref[fin]).max() <= 1e-5 * np.abs(m_ref[fin]).max()
+    # (m, l, acc) stands for sum e^s = l e^m: compare l and acc moved to the
+    # oracle's max. Each probability is exp2 of an fp32 fma on scores and a
+    # max of magnitude |m| log2(e), so its relative error grows like
+    # 4 * 2^-24 * |m| (on top of the 1e-5 of the small-logit tests).
+    shift = np.exp(m[fin] - m_ref[fin])
+    grow = 4 * 2.0 ** -24 * np.abs(m_ref[fin]).max()
+    assert normwise(l[fin] * shift, l_ref[fin]) <= 1e-5 + grow
+    assert normwise(acc[fin] * shift[:, None], acc_ref[fin]) <= bar + grow
+    o_ref, lse_ref = oracle.attention(q[:, :, None], k, v, scale)
+    assert normwise(np32(o), o_ref[:, :, 0]) <= bar
+    assert np.abs(np32(lse) - lse_ref[:, :, 0]).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
