@@ -190,16 +190,24 @@ def test_random_row_cascades(case):
 
 @pytest.mark.parametrize("sigma", [4.0, 8.0])
 @pytest.mark.parametrize("causal", [False, True])
-def test_large_logits_attention(sigma, causal):
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_large_logits_attention(sigma, causal, dtype):
     B, Hq, Hkv, L, d = 1, 4, 2, 333, 128
-    print_case(test="large_logits_attn", sigma=sigma, causal=causal)
-    q, k, v = inputs.attention_inputs(41, B, Hq, Hkv, L, L, d)
-    q = (q.float() * sigma).to(torch.bfloat16)
-    k = (k.float() * sigma).to(torch.bfloat16)
+    print_case(test="large_logits_attn", sigma=sigma, causal=causal, dtype=dtype)
+    q, k, v = inputs.attention_inputs(41, B, Hq, Hkv, L, L, d, dtype=dtype)
+    q = (q.float() * sigma).to(dtype)
+    k = (k.float() * sigma).to(dtype)
     scale = 1 / math.sqrt(d)
     o, lse = rf.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal=causal)
     o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal)
-    assert_bf16_attention(np32(o), o_ref, np32(lse), lse_ref, what=f"sigma={sigma}")
+    if dtype == torch.bfloat16:
+        assert_bf16_attention(np32(o), o_ref, np32(lse), lse_ref, what=f"sigma={sigma}")
+    else:
+        # fp32: the probabilities' relative error grows with the score
+        # magnitude (see the decode test below)
+        grow = 4 * 2.0 ** -24 * np.abs(lse_ref).max()
+        assert normwise(np32(o), o_ref) <= FP32_REL + grow
+        assert np.abs(np32(lse) - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
 
 
 @pytest.mark.parametrize("sigma", [4.0, 8.0])
