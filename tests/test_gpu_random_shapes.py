@@ -237,3 +237,37 @@ def test_large_logits_decode(sigma, dtype):
     o_ref, lse_ref = oracle.attention(q[:, :, None], k, v, scale)
     assert normwise(np32(o), o_ref[:, :, 0]) <= bar
     assert np.abs(np32(lse) - lse_ref[:, :, 0]).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_large_logits_mla(fused):
+    """Latent rows and queries scaled by 4: scores of standard deviation about 16."""
+    B, H, Lk, S = 2, 16, 1100, 5
+    print_case(test="large_logits_mla", fused=fused)
+    q, kv = inputs.mla_inputs(43, B, H, Lk)
+    q = (q.float() * 4).to(torch.bfloat16)
+    kv = (kv.float() * 4).to(torch.bfloat16)
+    scale = 1 / math.sqrt(576)
+    o, lse, _ = rf.mla_decode(q.to(DEV), kv.to(DEV), scale, S, out_dtype=torch.float32, fused=fused)
+    lat = kv[:, None]
+    o_ref, lse_ref = oracle.attention(q[:, :, None], lat, lat[..., :512], scale)
+    o_ref, lse_ref = o_ref[:, :, 0], lse_ref[:, :, 0]
+    grow = 4 * 2.0 ** -24 * np.abs(lse_ref).max()
+    assert (np.abs(np32(o) - o_ref).max(-1) / np.abs(o_ref).max(-1)).max() <= 1e-4 + grow
+    assert np.abs(np32(lse) - lse_ref).max() <= 1e-5 * np.abs(lse_ref).max()
+
+
+@pytest.mark.parametrize("spread", [100.0, 1e4])
+@pytest.mark.parametrize("renormalize", [True, False])
+def test_wide_logits_routing(spread, renormalize):
+    """Logits of standard deviation 100 and 10^4: all but a few probabilities
+    of each row underflow."""
+    print_case(test="wide_routing", spread=spread, renormalize=renormalize)
+    x = (inputs.routing_inputs(44, 300, 256).double() * spread).float()
+    w, idx = rf.softmax_topk(x.to(DEV), 8, renormalize)
+    w_ref, idx_ref = oracle.softmax_topk(x.numpy(), 8, renormalize)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    big = w_ref > 1e-30
+    w = np32(w)
+    assert (np.abs(w[big] - w_ref[big]) / w_ref[big]).max() <= 1e-5
+    assert np.abs(w[~big] - w_ref[~big]).max(initial=0.0) <= 1e-30
