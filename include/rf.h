@@ -80,7 +80,10 @@ typedef enum { RF_F32 = 0, RF_BF16 = 1, RF_DTYPE_MAX_ENUM_ = 0x7fffffff } rf_dty
  *   lse    [B, Hq, Lq] fp32 or NULL: m + ln(l) of the scaled scores.
  *   Hq % Hkv == 0; query head h reads key/value head h / (Hq / Hkv).
  *   causal != 0 masks key j for query i when j > i and needs Lq == Lk.
- *   Lk >= 1 whenever the output is non-empty. scale is explicit (no default).
+ *   Lk >= 1 whenever the output is non-empty. scale is explicit (no default)
+ *   and may be any finite value, zero and negative included (a zero scale
+ *   weights every unmasked key equally); a NaN or infinite scale returns
+ *   RF_ERR_INVALID_ARG. The same holds for every scale argument below.
  */
 rf_status rf_attn_fwd(rf_dtype dt, const void* q, const void* k, const void* v, void* o,
                       float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale,

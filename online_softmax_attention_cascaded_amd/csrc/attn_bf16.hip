@@ -77,11 +77,13 @@ struct Geo {
   static __device__ __forceinline__ int vswz(int row) { return D == 128 ? 2 * (row & 7) : 2 * (row & 3); }
 };
 
-template <int D, bool CAUSAL>
+// QX: the query bits go through (w & q_and) ^ q_xor (a scale <= 0); the
+// positive-scale instances leave them as they are.
+template <int D, bool CAUSAL, bool QX>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int BH,
-    int Hq, int Hkv, int Lq, int Lk, float c, int nqb) {
+    int Hq, int Hkv, int Lq, int Lk, float c, uint32_t q_and, uint32_t q_xor, int nqb) {
   using Gm = Geo<D>;
   constexpr int kRow = Gm::kRow, kTileBytes = Gm::kTileBytes, ND = Gm::ND, NDB = Gm::NDB;
   constexpr int NSM = Gm::NSM, NPV = Gm::NPV;
@@ -129,6 +131,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   for (int ds = 0; ds < ND; ++ds) {
     u32x4 w = {0u, 0u, 0u, 0u};
     if (qrow < Lq) w = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * D + 16 * ds + 8 * g);
+    if constexpr (QX) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (w[e] & q_and) ^ q_xor;  // sign / zero of the scale
+    }
     qf[ds] = __builtin_bit_cast(bf16x8, w);
   }
 
@@ -394,15 +400,22 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
                                 int causal, hipStream_t stream) {
   const int nqb = (Lq + BM - 1) / BM;
   const int BH = B * Hq;
-  const float c = scale * kLog2e;
+  const ScoreScale sc = score_scale(scale);
   dim3 grid(BH * (causal ? (nqb + 1) / 2 : nqb));
   auto qq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(k);
   auto vv = static_cast<const uint16_t*>(v);
   auto oo = static_cast<uint16_t*>(o);
-#define RF_ATTN_LAUNCH(D_, C_)                                                                 \
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, C_>), grid, dim3(256), 0, stream, qq, kk, vv, oo, \
-                     lse, BH, Hq, Hkv, Lq, Lk, c, nqb)
+  const bool qx = sc.q_and != ~0u || sc.q_xor != 0u;
+#define RF_ATTN_LAUNCH(D_, C_)                                                                     \
+  do {                                                                                            \
+    if (qx)                                                                                       \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, C_, true>), grid, dim3(256), 0, stream, qq, kk, \
+                         vv, oo, lse, BH, Hq, Hkv, Lq, Lk, sc.c, sc.q_and, sc.q_xor, nqb);         \
+    else                                                                                          \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D_, C_, false>), grid, dim3(256), 0, stream, qq,  \
+                         kk, vv, oo, lse, BH, Hq, Hkv, Lq, Lk, sc.c, sc.q_and, sc.q_xor, nqb);     \
+  } while (0)
   if (d == 64) {
     if (causal) RF_ATTN_LAUNCH(64, true); else RF_ATTN_LAUNCH(64, false);
   } else {

@@ -136,7 +136,8 @@ template <int NST, bool MERGE>
 __global__ __launch_bounds__(512, NST == 2 ? 2 : 1) void mla_decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, float* __restrict__ part_m,
     float* __restrict__ part_l, float* __restrict__ part_acc, int H, int Lk, int S, int seg_len,
-    float c, int* __restrict__ counters, void* __restrict__ o, float* __restrict__ lse, int out_bf16) {
+    float c, uint32_t q_and, uint32_t q_xor, int* __restrict__ counters, void* __restrict__ o,
+    float* __restrict__ lse, int out_bf16) {
   __shared__ __attribute__((aligned(1024))) char smem[smem_bytes<NST>()];
   // Flag of the fused merge, in the stage memory: written only after the last
   // stage has been consumed. (A second LDS object would make the compiler
@@ -182,6 +183,8 @@ __global__ __launch_bounds__(512, NST == 2 ? 2 : 1) void mla_decode_split_kernel
       const int ks = (j < 4) ? 4 * dq + j : 16 + (j - 4);  // global k-step (16, 17 = positional)
       u32x4 w = {0u, 0u, 0u, 0u};
       if (j < nks) w = *reinterpret_cast<const u32x4*>(qr + 32 * ks + 8 * g4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (w[e] & q_and) ^ q_xor;  // sign / zero of the scale
       qf[j] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
@@ -391,12 +394,13 @@ hipError_t launch_mla_decode_split(const void* q, const void* kv, float* part_m,
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) cu_count[dev].store(cus, std::memory_order_relaxed);
   }
+  const ScoreScale sc = score_scale(scale);
   auto qq = static_cast<const uint16_t*>(q);
   auto kk = static_cast<const uint16_t*>(kv);
 #define RF_MLA_LAUNCH(NST_, MERGE_)                                                                  \
   hipLaunchKernelGGL((mla_decode_split_kernel<NST_, MERGE_>), grid, dim3(512), 0, stream, qq, kk,     \
-                     part_m, part_l, part_acc, H, Lk, S, seg_len, scale * kLog2e, counters, o, lse,    \
-                     out_bf16)
+                     part_m, part_l, part_acc, H, Lk, S, seg_len, sc.c, sc.q_and, sc.q_xor, counters, \
+                     o, lse, out_bf16)
   const bool two_stage = (long long)grid.x > cus;
   if (counters) {
     if (two_stage) RF_MLA_LAUNCH(2, true); else RF_MLA_LAUNCH(4, true);

@@ -72,7 +72,7 @@ rf_status rf_attn_fwd(rf_dtype dt, const void* q, const void* k, const void* v, 
   RF_REQUIRE(q && k && v && o, RF_ERR_INVALID_ARG, "rf_attn_fwd: null tensor pointer");
   RF_REQUIRE(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(o, 16) && aligned(lse, 4),
              RF_ERR_INVALID_ARG, "rf_attn_fwd: pointers must be 16-byte aligned");
-  RF_REQUIRE(scale == scale, RF_ERR_INVALID_ARG, "rf_attn_fwd: scale is NaN");
+  RF_REQUIRE(__builtin_isfinite(scale), RF_ERR_INVALID_ARG, "rf_attn_fwd: scale is not finite");
   RF_REQUIRE(prod({B, Hq, Lq > Lk ? Lq : Lk, d}) < kMaxElems, RF_ERR_INVALID_ARG,
              "rf_attn_fwd: problem too large");
   if (dt == RF_F32) {
@@ -105,7 +105,7 @@ rf_status rf_attn_decode_split(rf_dtype dt, const void* q, const void* k, const 
   RF_REQUIRE(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(part_acc, 16) &&
                  aligned(part_m, 4) && aligned(part_l, 4),
              RF_ERR_INVALID_ARG, "rf_attn_decode_split: pointers must be 16-byte aligned");
-  RF_REQUIRE(scale == scale, RF_ERR_INVALID_ARG, "rf_attn_decode_split: scale is NaN");
+  RF_REQUIRE(__builtin_isfinite(scale), RF_ERR_INVALID_ARG, "rf_attn_decode_split: scale is not finite");
   RF_REQUIRE(prod({B, Hkv, Lk, d}) < kMaxElems && prod({B, Hq, S, d}) < kMaxElems && prod({B, Hkv, S}) < kMaxGrid,
              RF_ERR_INVALID_ARG, "rf_attn_decode_split: problem too large");
   RF_REQUIRE(d == 64 || d == 128, RF_ERR_UNSUPPORTED, "rf_attn_decode_split: head size %d (need 64 or 128)", d);
@@ -135,7 +135,7 @@ rf_status check_mla(const char* fn, const void* q, const void* kv, float* part_m
   RF_REQUIRE(aligned(q, 16) && aligned(kv, 16) && aligned(part_acc, 16) && aligned(part_m, 4) &&
                  aligned(part_l, 4),
              RF_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
-  RF_REQUIRE(scale == scale, RF_ERR_INVALID_ARG, "%s: scale is NaN", fn);
+  RF_REQUIRE(__builtin_isfinite(scale), RF_ERR_INVALID_ARG, "%s: scale is not finite", fn);
   RF_REQUIRE(Dqk == 576 && Dv == 512, RF_ERR_UNSUPPORTED,
              "%s: widths %d/%d (need 576 for keys, 512 for values)", fn, Dqk, Dv);
   RF_REQUIRE(H % 16 == 0 && H <= 128, RF_ERR_UNSUPPORTED,

@@ -40,6 +40,22 @@ __device__ __forceinline__ u32x4 buf_load16_stream(__amdgpu_buffer_rsrc_t r, int
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// The scale of the scores, in the form the MFMA kernels use it: a positive
+// factor c (exp2 units) and a transform of the bf16 query bits (w & q_and) ^
+// q_xor. A negative scale flips the sign of every query value (exact), so
+// the scaled scores are the same while c stays positive and the running
+// maxima, the masking to -inf and the lazy reference keep their meaning; a
+// zero scale zeroes the query, so every score is exactly 0.
+struct ScoreScale {
+  float c;
+  uint32_t q_and, q_xor;
+};
+inline ScoreScale score_scale(float scale) {
+  if (scale > 0.f) return {scale * kLog2e, ~0u, 0u};
+  if (scale < 0.f) return {-scale * kLog2e, ~0u, 0x80008000u};
+  return {kLog2e, 0u, 0u};
+}
 constexpr float kNegInf = -__builtin_inff();
 
 // Workgroup barrier for handing LDS contents between waves. It waits for this

@@ -69,6 +69,9 @@ int main() {
   EXPECT(attn(RF_BF16, F, F, 1, 4, 2, 64, 32, 128, 0.1f, 1), INV, 0);
   EXPECT(attn(RF_BF16, F, MIS, 1, 4, 2, 64, 64, 128, 0.1f, 0), INV, 0);
   EXPECT(attn(RF_BF16, F, F, 1, 4, 2, 64, 64, 128, NAN, 0), INV, 0);
+  EXPECT(attn(RF_BF16, F, F, 1, 4, 2, 64, 64, 128, INFINITY, 0), INV, 0);
+  EXPECT(attn(RF_BF16, F, F, 1, 4, 2, 64, 64, 128, 0.f, 0), OK, 1);
+  EXPECT(attn(RF_BF16, F, F, 1, 4, 2, 64, 64, 128, -0.5f, 1), OK, 1);
   EXPECT(attn(RF_BF16, F, F, 1, 4, 2, 64, 64, 96, 0.1f, 0), UNS, 0);
   EXPECT(attn(RF_BF16, F, F, BIG, BIG, 1, BIG, BIG, 128, 0.1f, 0), INV, 0);    // too large
   EXPECT(attn(RF_BF16, F, F, 1, BIG, BIG, BIG, BIG, BIG, 0.1f, 0), INV, 0);

@@ -79,6 +79,8 @@ def attn(lib, dt=BF16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=
         (dict(q=None), INVALID),
         (dict(o=MISALIGNED), INVALID),
         (dict(scale=float("nan")), INVALID),
+        (dict(scale=float("inf")), INVALID),
+        (dict(scale=float("-inf")), INVALID),
         (dict(d=96), UNSUPPORTED),
         (dict(dt=F32, d=96), UNSUPPORTED),
         (dict(d=32), UNSUPPORTED),
@@ -112,6 +114,8 @@ def decode(lib, dt=BF16, q=FAKE, k=FAKE, v=FAKE, m=FAKE, l=FAKE, acc=FAKE, B=1, 
         (dict(k=MISALIGNED), INVALID),
         (dict(dt=7), INVALID),
         (dict(scale=float("nan")), INVALID),
+        (dict(scale=float("inf")), INVALID),
+        (dict(scale=float("-inf")), INVALID),
         (dict(d=96), UNSUPPORTED),
         (dict(dt=F32, d=32), UNSUPPORTED),
         (dict(Hq=34, Hkv=2), UNSUPPORTED),
@@ -146,6 +150,8 @@ def mla(lib, q=FAKE, kv=FAKE, m=FAKE, l=FAKE, acc=FAKE, B=2, H=16, Lk=100, Dqk=5
         (dict(acc=None), INVALID),
         (dict(kv=MISALIGNED), INVALID),
         (dict(scale=float("nan")), INVALID),
+        (dict(scale=float("inf")), INVALID),
+        (dict(scale=float("-inf")), INVALID),
         (dict(Dqk=192, Dv=128), UNSUPPORTED),
         (dict(Dv=256), UNSUPPORTED),
         (dict(H=8), UNSUPPORTED),

@@ -271,3 +271,46 @@ def test_wide_logits_routing(spread, renormalize):
     w = np32(w)
     assert (np.abs(w[big] - w_ref[big]) / w_ref[big]).max() <= 1e-5
     assert np.abs(w[~big] - w_ref[~big]).max(initial=0.0) <= 1e-30
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0, -0.125, -2.0])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_zero_and_negative_scale(scale, dtype):
+    """Scale 0 (every unmasked key weighted equally: O is the mean of V, lse =
+    ln of the key count) and negative scales, for prefill in both modes (a
+    ragged last key tile and the causal diagonal are masked) and for decode."""
+    B, Hq, Hkv, L, d = 1, 4, 2, 200, 128
+    print_case(test="odd_scale", scale=scale, dtype=dtype)
+    q, k, v = inputs.attention_inputs(45, B, Hq, Hkv, L, L, d, dtype=dtype)
+    for causal in (False, True):
+        o, lse = rf.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale, causal=causal)
+        o_ref, lse_ref = oracle.attention(q, k, v, scale, causal=causal)
+        if dtype == torch.bfloat16:
+            assert_bf16_attention(np32(o), o_ref, np32(lse), lse_ref, what=f"scale={scale} causal={causal}")
+        else:
+            grow = 4 * 2.0 ** -24 * np.abs(lse_ref).max()
+            assert normwise(np32(o), o_ref) <= FP32_REL + grow
+            assert np.abs(np32(lse) - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+        if scale == 0.0:
+            n_keys = np.arange(1, L + 1) if causal else np.full(L, L)
+            assert np.abs(np32(lse) - np.log(n_keys)).max() <= 1e-5 * math.log(L)
+    qd = q[:, :, 0].contiguous()
+    o, lse, _ = rf.attn_decode(qd.to(DEV), k.to(DEV), v.to(DEV), scale, 3, out_dtype=torch.float32)
+    o_ref, lse_ref = oracle.attention(qd[:, :, None], k, v, scale)
+    bar = 1e-4 if dtype == torch.bfloat16 else FP32_REL
+    assert normwise(np32(o), o_ref[:, :, 0]) <= bar
+    assert np.abs(np32(lse) - lse_ref[:, :, 0]).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.05])
+@pytest.mark.parametrize("fused", [False, True])
+def test_zero_and_negative_scale_mla(scale, fused):
+    B, H, Lk, S = 2, 16, 700, 3
+    print_case(test="odd_scale_mla", scale=scale, fused=fused)
+    q, kv = inputs.mla_inputs(46, B, H, Lk)
+    o, lse, _ = rf.mla_decode(q.to(DEV), kv.to(DEV), scale, S, out_dtype=torch.float32, fused=fused)
+    lat = kv[:, None]
+    o_ref, lse_ref = oracle.attention(q[:, :, None], lat, lat[..., :512], scale)
+    o_ref, lse_ref = o_ref[:, :, 0], lse_ref[:, :, 0]
+    assert (np.abs(np32(o) - o_ref).max(-1) / np.abs(o_ref).max(-1)).max() <= 1e-4
+    assert np.abs(np32(lse) - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
