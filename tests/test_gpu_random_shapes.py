@@ -314,3 +314,47 @@ def test_zero_and_negative_scale_mla(scale, fused):
     o_ref, lse_ref = o_ref[:, :, 0], lse_ref[:, :, 0]
     assert (np.abs(np32(o) - o_ref).max(-1) / np.abs(o_ref).max(-1)).max() <= 1e-4
     assert np.abs(np32(lse) - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+
+
+@pytest.mark.parametrize("d", [4, 100, 128, 260, 512, 1024])
+@pytest.mark.parametrize("S", [1, 2, 9, 33])
+def test_merge_widths(d, S):
+    """The merge at every supported width class (one 128-column block or
+    several, a partial block) and segment counts, with empty states mixed in;
+    bf16 and fp32 outputs."""
+    print_case(test="merge_widths", d=d, S=S)
+    rng = np.random.default_rng(100 + d + S)
+    rows = 19
+    m = (rng.standard_normal((rows, S)) * 4).astype(np.float32)
+    l = rng.uniform(0.5, 50, (rows, S)).astype(np.float32)
+    acc = rng.standard_normal((rows, S, d)).astype(np.float32)
+    m[rng.random((rows, S)) < 0.3] = -np.inf
+    m[3] = -np.inf
+    l[np.isinf(m)] = 0
+    acc[np.isinf(m)] = 0
+    o_ref, lse_ref = oracle.merge_states(m, l, acc)
+    args = [torch.from_numpy(x).to(DEV) for x in (m, l, acc)]
+    o, lse = rf.merge_states(*args, out_dtype=torch.float32)
+    assert normwise(np32(o), o_ref) <= FP32_REL
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(np32(lse)), fin)
+    assert np.abs(np32(lse)[fin] - lse_ref[fin]).max() <= 1e-5 * max(1, np.abs(lse_ref[fin]).max())
+    o16, _ = rf.merge_states(*args, out_dtype=torch.bfloat16)
+    assert np.abs(np32(o16) - o_ref).max() <= 2 ** -8 * max(1e-30, np.abs(o_ref).max())
+
+
+@pytest.mark.parametrize("Lk,S", [(1, 1), (3, 8), (31, 4), (33, 2), (97, 12)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_mla_short_caches(Lk, S, fused):
+    """Latent caches shorter than a step or than the segment count (empty
+    segments), in both launch forms."""
+    B, H = 2, 16
+    print_case(test="mla_short", Lk=Lk, S=S, fused=fused)
+    q, kv = inputs.mla_inputs(47, B, H, Lk)
+    scale = 1 / math.sqrt(576)
+    o, lse, _ = rf.mla_decode(q.to(DEV), kv.to(DEV), scale, S, out_dtype=torch.float32, fused=fused)
+    lat = kv[:, None]
+    o_ref, lse_ref = oracle.attention(q[:, :, None], lat, lat[..., :512], scale)
+    o_ref, lse_ref = o_ref[:, :, 0], lse_ref[:, :, 0]
+    assert (np.abs(np32(o) - o_ref).max(-1) / np.abs(o_ref).max(-1)).max() <= 1e-4
+    assert np.abs(np32(lse) - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
