@@ -358,3 +358,23 @@ def test_mla_short_caches(Lk, S, fused):
     o_ref, lse_ref = o_ref[:, :, 0], lse_ref[:, :, 0]
     assert (np.abs(np32(o) - o_ref).max(-1) / np.abs(o_ref).max(-1)).max() <= 1e-4
     assert np.abs(np32(lse) - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
+
+
+@pytest.mark.parametrize("renormalize", [True, False])
+@pytest.mark.parametrize("E,k", [(256, 8), (64, 4), (1024, 16)])
+def test_routing_masked_experts(renormalize, E, k):
+    """Experts masked with -inf logits (a common way to disable experts): every
+    row keeps at least k finite logits, so the masked ones are never chosen
+    and weigh nothing in the denominator."""
+    print_case(test="routing_masked", E=E, k=k, renormalize=renormalize)
+    rng = np.random.default_rng(48 + E)
+    x = inputs.routing_inputs(49, 101, E).numpy().copy()
+    for r in range(x.shape[0]):
+        n_masked = int(rng.integers(0, E - k + 1))
+        x[r, rng.choice(E, size=n_masked, replace=False)] = -np.inf
+    x = torch.from_numpy(x)
+    w, idx = rf.softmax_topk(x.to(DEV), k, renormalize)
+    w_ref, idx_ref = oracle.softmax_topk(x.numpy(), k, renormalize)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.all(np.isfinite(x.numpy()[np.arange(x.shape[0])[:, None], idx.cpu().numpy()]))
+    assert (np.abs(np32(w) - w_ref) / w_ref).max() <= 1e-5
