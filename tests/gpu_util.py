@@ -44,6 +44,19 @@ def assert_bf16_attention(o, o_ref, lse=None, lse_ref=None, what=""):
         assert lerr <= LSE_ABS, f"{what}: lse max abs error {lerr}"
 
 
+def assert_fp8_entries(c, c_ref, mag, units, what=""):
+    """Every entry of an FP8 GEMM result against the fp64 oracle:
+    |c - c_ref| <= 2^-8 |c_ref| + units * 2^-23 * mag, where mag is
+    s_i t_j sum_k |a_ik b_jk| (the sum the fp32 accumulation rounds along) and
+    units counts the fp32 roundings (K additions, the scale products and, for
+    the running scale, the accumulator rescales); 2^-8 is the bf16 output
+    rounding."""
+    c = np.asarray(c, np.float64)
+    tol = 2.0 ** -8 * np.abs(c_ref) + units * 2.0 ** -23 * mag
+    bad = np.argwhere(np.abs(c - c_ref) > tol)
+    assert len(bad) == 0, f"{what}: {len(bad)} entries outside the bound, first {bad[:3].tolist()}"
+
+
 def print_case(**kw):
     print("case " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
 

@@ -1,7 +1,8 @@
-"""GPU parity of the FP8 cascade (rf_absmax_quant_fp8, rf_absmax_quant_gemm_fp8)
-through the C ABI: quantised codes and scales bit-exact against the oracle, the
-GEMM within 3e-2 relative Frobenius error of the oracle's fp64 result for the
-same quantised operands."""
+"""GPU parity of the FP8 cascade (rf_absmax_quant_fp8, rf_absmax_quant_gemm_fp8,
+and the one-pass running-scale form) through the C ABI: quantised codes and
+scales bit-exact against the oracle, the GEMM within 3e-2 relative Frobenius
+error of the oracle's fp64 result for the same quantised operands, and every
+entry of C within the fp32-accumulation bound of assert_fp8_entries."""
 
 import numpy as np
 import pytest
@@ -10,7 +11,7 @@ import torch
 import oracle
 import online_softmax_attention_cascaded_amd as rf
 from online_softmax_attention_cascaded_amd import inputs
-from gpu_util import DEV, FP8_REL_FRO, needs_gpu, np32, print_case, rel_fro
+from gpu_util import DEV, FP8_REL_FRO, assert_fp8_entries, needs_gpu, np32, print_case, rel_fro
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -92,8 +93,28 @@ def test_gemm_small(M, N, K):
     assert np.array_equal(aq.cpu().numpy(), aq_ref) and np.array_equal(sa.cpu().numpy(), sa_ref)
     c_ref = oracle.quant_gemm(aq_ref, sa_ref, bq.cpu().numpy(), bs.cpu().numpy())
     assert rel_fro(np32(c), c_ref) <= FP8_REL_FRO
-    # Much tighter in fact: fp32 accumulation + one bf16 rounding.
+    # Much tighter in fact: fp32 accumulation + one bf16 rounding, entry by entry.
     assert rel_fro(np32(c), c_ref) <= 5e-3
+    assert_fp8_entries(np32(c), c_ref, two_pass_magnitude(aq_ref, sa_ref, bq.cpu().numpy(), bs.cpu().numpy()),
+                       K + 4, f"gemm {M}x{N}x{K}")
+
+
+def two_pass_magnitude(aq, sa, bq, bs):
+    """s_i t_j sum_k |a_ik b_jk| over the e4m3 codes (exact in fp64)."""
+    ma, mb = np.abs(oracle.e4m3_decode(aq)), np.abs(oracle.e4m3_decode(bq))
+    return sa.astype(np.float64)[:, None] * bs.astype(np.float64)[None, :] * (ma @ mb.T)
+
+
+def running_magnitude(x, bq, bs):
+    """The one-pass sum over absolute values: the running-scale oracle on |A|
+    and |B| (the codes of |x| are the magnitudes of the codes of x, and the
+    scales, running ones included, are the same)."""
+    return oracle.quant_gemm_running_scale(np.abs(x), bq & 0x7F, bs, K_TILE)
+
+
+def running_units(K):
+    """K additions, at most K / 64 rescales of three roundings each, scales."""
+    return K + 3 * K // K_TILE + 4
 
 
 # ---- one-pass form with a running per-row scale (K tiles of 64 columns)
@@ -115,9 +136,11 @@ def _running_case(a, bsrc):
 def test_running_scale_gemm_small(M, N, K):
     print_case(test="gemm_running", M=M, N=N, K=K)
     a, bsrc = inputs.quant_inputs(12, M, N, K)
-    c, c_ref, sa, sa_ref, _, _ = _running_case(a, bsrc)
+    c, c_ref, sa, sa_ref, bq, bs = _running_case(a, bsrc)
     assert np.array_equal(sa, sa_ref)          # the final running scale is the row's scale
     assert rel_fro(c, c_ref) <= 5e-3
+    assert_fp8_entries(c, c_ref, running_magnitude(a.float().numpy(), bq.cpu().numpy(), bs.cpu().numpy()),
+                       running_units(K), f"running {M}x{N}x{K}")
 
 
 def test_running_scale_tiny_scales():
@@ -135,10 +158,12 @@ def test_running_scale_tiny_scales():
     a[24, :512] *= 1e-36
     a[25, 512:] *= 1e-36
     print_case(test="gemm_running_tiny")
-    c, c_ref, sa, sa_ref, _, _ = _running_case(a, bsrc)
+    c, c_ref, sa, sa_ref, bq, bs = _running_case(a, bsrc)
     assert np.array_equal(sa, sa_ref)
     for r in range(M):
         assert rel_fro(c[r], c_ref[r]) <= 5e-3, r
+    assert_fp8_entries(c, c_ref, running_magnitude(a.float().numpy(), bq.cpu().numpy(), bs.cpu().numpy()),
+                       running_units(K), "running, tiny scales")
 
 
 def test_running_scale_growth_and_zero_rows():
@@ -152,9 +177,11 @@ def test_running_scale_growth_and_zero_rows():
     a[3, -1] = 1000.0
     a[4, 5 * K_TILE + 3] = -300.0
     print_case(test="gemm_running_growth")
-    c, c_ref, sa, sa_ref, _, _ = _running_case(a, bsrc)
+    c, c_ref, sa, sa_ref, bq, bs = _running_case(a, bsrc)
     assert np.array_equal(sa, sa_ref)
     assert np.all(c[1] == 0)
     assert rel_fro(c, c_ref) <= 5e-3
     for r in (2, 3, 4):
         assert rel_fro(c[r], c_ref[r]) <= 5e-3
+    assert_fp8_entries(c, c_ref, running_magnitude(a.float().numpy(), bq.cpu().numpy(), bs.cpu().numpy()),
+                       running_units(K), "running, growth and zero rows")

@@ -16,9 +16,10 @@ import torch
 import oracle
 import online_softmax_attention_cascaded_amd as rf
 from online_softmax_attention_cascaded_amd import inputs
-from gpu_util import (DEV, FP32_REL, assert_bf16_attention, needs_gpu, normwise, np32,
-                      print_case, rel_fro)
+from gpu_util import (DEV, FP32_REL, assert_bf16_attention, assert_fp8_entries, needs_gpu, normwise,
+                      np32, print_case, rel_fro)
 from test_gpu_decode import _check_partials
+from test_gpu_fp8 import running_magnitude, running_units, two_pass_magnitude
 from test_gpu_moments import _compare as _compare_moments
 from test_gpu_softmax import _compare as _compare_softmax
 
@@ -144,12 +145,16 @@ def test_random_fp8_gemms(case):
     aq_ref, sa_ref = oracle.absmax_quant(a.float().numpy())
     assert np.array_equal(sa.cpu().numpy(), sa_ref)
     assert np.array_equal(aq.cpu().numpy(), aq_ref)
-    c_ref = oracle.quant_gemm(aq_ref, sa_ref, bq.cpu().numpy(), bs.cpu().numpy())
+    bqh, bsh = bq.cpu().numpy(), bs.cpu().numpy()
+    c_ref = oracle.quant_gemm(aq_ref, sa_ref, bqh, bsh)
     assert rel_fro(np32(c), c_ref) <= 5e-3
+    assert_fp8_entries(np32(c), c_ref, two_pass_magnitude(aq_ref, sa_ref, bqh, bsh), K + 4, "two-pass")
     c2, sa2 = rf.absmax_quant_gemm_fp8_running(a.to(DEV), bq, bs)
-    c2_ref = oracle.quant_gemm_running_scale(a.float().numpy(), bq.cpu().numpy(), bs.cpu().numpy(), 64)
+    x = a.float().numpy()
+    c2_ref = oracle.quant_gemm_running_scale(x, bqh, bsh, 64)
     assert np.array_equal(sa2.cpu().numpy(), sa_ref)
     assert rel_fro(np32(c2), c2_ref) <= 5e-3
+    assert_fp8_entries(np32(c2), c2_ref, running_magnitude(x, bqh, bsh), running_units(K), "running")
 
 
 @pytest.mark.parametrize("case", MLA, ids=str)
