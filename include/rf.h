@@ -42,6 +42,9 @@
  *   - A call whose output is empty (a zero batch or row count) returns RF_OK
  *     and enqueues nothing; null pointers are accepted only then.
  *   - Calls are re-entrant; rf_last_error() is per host thread.
+ *   - A call enqueues kernels only (no allocation, memset, copy or host
+ *     synchronisation), so it can be recorded into a HIP graph by stream
+ *     capture and replayed; a replay reads the buffers' contents at that time.
  *   - Inputs are expected finite; a NaN propagates to the rows it touches.
  */
 #ifndef RF_H_
