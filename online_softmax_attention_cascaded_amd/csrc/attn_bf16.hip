@@ -32,6 +32,8 @@
 #include "rf_device.hpp"
 #include "rf_launch.hpp"
 
+#include <type_traits>
+
 namespace rf {
 namespace {
 
@@ -217,8 +219,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 
   // One tile: softmax of tile t (scores `cur`) and O += V(t) P(t), with the
   // scores of tile t+1 computed into `nxt` in the same instruction stream so
-  // the matrix cores work while the exponentials run on the VALU.
-  auto tile = [&](int t, Scores& cur, Scores& nxt, const char* knext, const char* vb) {
+  // the matrix cores work while the exponentials run on the VALU (NEXT; a
+  // causal wave's last tile leaves them out).
+  auto tile = [&](auto next_c, int t, Scores& cur, Scores& nxt, const char* knext, const char* vb) {
+    constexpr bool NEXT = decltype(next_c)::value;
     const int t0 = t * BN;
     const bool need_mask = (t0 + BN > Lk) || (CAUSAL && t0 + BN - 1 > q0 + wave * 32);
     if (need_mask) {
@@ -275,20 +279,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     // than equal priority (the reverse, or priority only for the VALU
     // instructions inside this block, measured slower).
     __builtin_amdgcn_s_setprio(1);
-    nxt.s0 = f32x16{};
-    nxt.s1 = f32x16{};
+    if constexpr (NEXT) {
+      nxt.s0 = f32x16{};
+      nxt.s1 = f32x16{};
+    }
     bf16x8 kf[KA + 1];
     auto kread = [&](int i) {
       return *reinterpret_cast<const bf16x8*>(knext + kr[i >> 1] + (i & 1) * 32 * kRow);
     };
 #pragma unroll
-    for (int i = 0; i < KA; ++i) kf[i] = kread(i);
+    for (int i = 0; i < KA; ++i)
+      if constexpr (NEXT) kf[i] = kread(i);
     u32x4 pw[4];
     float rs = 0.f;
     constexpr int EV = 16 / NSM;  // probability pairs per score MFMA
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i % EV == 0) {
+      if (NEXT && i % EV == 0) {
         const int m = i / EV;
         if (m + KA < NSM) kf[(m + KA) % (KA + 1)] = kread(m + KA);
         if (m & 1)
@@ -360,12 +367,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   // Iteration t: LDS holds K(t+1) and V(t); it loads K(t+2) and V(t+1) into the
   // buffers that held K(t) and V(t-1), both consumed before the last barrier.
   // At the last tile the scores of the (absent) next tile are computed from
-  // stale LDS data and never used.
+  // stale LDS data and never used, except in causal attention, where a wave
+  // leaves out the scores of a tile it will not process (its last tile of
+  // each query block: 1-2 % of the causal time, identical output; for the
+  // non-causal kernel the second form raised register use into spills).
   auto iter = [&](int t, Scores& cur, Scores& nxt, char* kcur, char* knext, char* vcur,
                   char* vnext) {
     if (t + 2 < ntiles) load_k(t + 2, kcur);
     if (t + 1 < ntiles) load_v(t + 1, vnext);
-    if (active(t)) tile(t, cur, nxt, knext, vcur);
+    if (active(t)) {
+      if constexpr (!CAUSAL) {
+        tile(std::true_type{}, t, cur, nxt, knext, vcur);
+      } else {
+        if (t + 1 < ntiles && active(t + 1))
+          tile(std::true_type{}, t, cur, nxt, knext, vcur);
+        else
+          tile(std::false_type{}, t, cur, nxt, knext, vcur);
+      }
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
   };
